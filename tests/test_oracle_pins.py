@@ -1,0 +1,526 @@
+"""Pins of the CPU oracle against facts fixed outside it: IEEE fp16 rounding,
+exact arithmetic, textbook closed forms of the delta rule, Proposition 1 of
+the STEPQuant essay, brute-force quantization, the storage accounting the
+essay prints, and brute-force top-K.  None of these re-types the oracle's
+formulas; each is chosen so that a plausible mistake (a dropped term, a wrong
+sign, a transposed operand, a wrong bit position) fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from tests import slotcodec
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")
+
+
+def _cfg(ora, H=1, dk=16, dv=16, keyrow=False, gate_vec=False, rf16=True, cf16=True,
+         window=1, comps=0, bits=None, width=8):
+    if bits is None:
+        bits = np.full(H * dk if keyrow else H, width, dtype=np.uint8)
+    return ora.Cfg(H, dk, dv, keyrow, gate_vec, rf16, cf16, window, comps, bits)
+
+
+# ------------------------------------------------------------ fp16 rounding
+
+def test_fp16_matches_ieee_nearest_even(ora):
+    """Strided sweep of all float32 patterns plus every pattern next to an fp16
+    rounding boundary, against numpy's IEEE half conversion."""
+    rng = np.random.default_rng(0)
+    pats = [np.arange(0, 2 ** 32, 9973, dtype=np.uint64).astype(np.uint32)]
+    # patterns whose low 13 mantissa bits sit at / beside the half-way point
+    hi = rng.integers(0, 2 ** 19, size=200_000, dtype=np.uint64) << np.uint64(13)
+    for low in (0x0FFF, 0x1000, 0x1001, 0x0000, 0x1FFF):
+        pats.append((hi | np.uint64(low)).astype(np.uint32))
+    # subnormal fp16 region and overflow edge
+    pats.append(np.arange(0x33000000, 0x38900000, 37, dtype=np.uint32))
+    pats.append(np.arange(0x477FE000, 0x47800100, 1, dtype=np.uint32))
+    x = np.concatenate(pats).view(np.float32)
+    x = x[np.isfinite(x)]
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    got = ora.f32_to_f16(x)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (x[bad[:5]], got[bad[:5]], want[bad[:5]])
+    back = ora.f16_to_f32(np.arange(0, 2 ** 16, dtype=np.uint32).astype(np.uint16))
+    ref = np.arange(0, 2 ** 16, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    same = (back == ref) | (np.isnan(back) & np.isnan(ref))
+    assert same.all()
+
+
+# ------------------------------------------------------------ canonical sum
+
+def test_csum_exact_on_integers(ora):
+    """With small integer terms every partial sum is exact, so the canonical sum
+    must equal the exact dot product (a dropped or doubled term fails)."""
+    rng = np.random.default_rng(1)
+    for n in (8, 16, 64, 128):
+        for _ in range(50):
+            x = rng.integers(-300, 300, n).astype(np.float32)
+            y = rng.integers(-300, 300, n).astype(np.float32)
+            assert float(ora.csum(x, y)) == float(np.dot(x.astype(np.int64), y.astype(np.int64)))
+
+
+def test_csum_error_bound(ora):
+    """|csum - exact| <= n * 2^-24 * sum|x y| (standard dot-product bound)."""
+    rng = np.random.default_rng(2)
+    for n in (64, 128):
+        for _ in range(200):
+            x = rng.standard_normal(n).astype(np.float32)
+            y = rng.standard_normal(n).astype(np.float32)
+            exact = np.dot(x.astype(np.float64), y.astype(np.float64))
+            bound = n * 2.0 ** -24 * np.sum(np.abs(x.astype(np.float64) * y))
+            assert abs(float(ora.csum(x, y)) - exact) <= bound
+
+
+# ------------------------------------------------- unquantized closed forms
+
+def _orthonormal(rng, d, n):
+    q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    return q[:, :n].T  # n orthonormal rows
+
+
+@pytest.mark.parametrize("prec", ["f64", "f32"])
+def test_delta_rule_retrieval_closed_form(ora, prec):
+    """a = 1, beta = 1, orthonormal keys: after writing (k_m, v_m), reading with
+    q = k_m returns v_m exactly (delta-rule associative memory)."""
+    rng = np.random.default_rng(3)
+    dk, dv, n = 32, 24, 12
+    keys = _orthonormal(rng, dk, n)
+    vals = rng.standard_normal((n, dv))
+    dt = np.float64 if prec == "f64" else np.float32
+    step = ora.step_f64 if prec == "f64" else ora.step_f32
+    M = np.zeros((dk, dv), dtype=dt)
+    for m in range(n):
+        step(M, keys[m].astype(dt), keys[m].astype(dt), vals[m].astype(dt), np.ones(1), 1.0, False)
+    tol = 1e-12 if prec == "f64" else 2e-5
+    for m in range(n):
+        o = step(M.copy(), keys[m].astype(dt), np.zeros(dk, dt), np.zeros(dv, dt), np.ones(1), 0.0, False)
+        np.testing.assert_allclose(o, vals[m], atol=tol, rtol=0)
+
+
+def test_gated_retrieval_closed_form(ora):
+    """Scalar gates a_t: reading key k_m after step T gives prod_{s>m} a_s * v_m."""
+    rng = np.random.default_rng(4)
+    dk, dv, n = 16, 8, 10
+    keys = _orthonormal(rng, dk, n)
+    vals = rng.standard_normal((n, dv))
+    gates = rng.uniform(0.7, 1.0, n)
+    M = np.zeros((dk, dv))
+    for m in range(n):
+        ora.step_f64(M, keys[m], keys[m], vals[m], gates[m:m + 1], 1.0, False)
+    for m in range(n):
+        o = ora.step_f64(M.copy(), keys[m], np.zeros(dk), np.zeros(dv), np.ones(1), 0.0, False)
+        np.testing.assert_allclose(o, np.prod(gates[m + 1:]) * vals[m], atol=1e-12, rtol=0)
+
+
+def test_keyvec_gate_one_hot_keys(ora):
+    """KDA gate on one-hot keys: each key row decays by its own gate product,
+    and a repeated key overwrites (beta = 1)."""
+    rng = np.random.default_rng(5)
+    dk, dv = 8, 6
+    seq = [3, 5, 1, 3]
+    vals = rng.standard_normal((len(seq), dv))
+    gates = rng.uniform(0.8, 1.0, (len(seq), dk))
+    M = np.zeros((dk, dv))
+    for t, i in enumerate(seq):
+        e = np.eye(dk)[i]
+        ora.step_f64(M, e, e, vals[t], gates[t], 1.0, True)
+    # row 3 was overwritten at the last step; rows 5 and 1 decayed since written
+    np.testing.assert_allclose(M[3], vals[3], atol=1e-12)
+    np.testing.assert_allclose(M[5], vals[1] * gates[2, 5] * gates[3, 5], atol=1e-12)
+    np.testing.assert_allclose(M[1], vals[2] * gates[3, 1], atol=1e-12)
+    assert np.all(M[[0, 2, 4, 6, 7]] == 0)
+
+
+def test_f32_path_tracks_f64(ora):
+    rng = np.random.default_rng(6)
+    dk = dv = 64
+    M32 = np.zeros((dk, dv), np.float32)
+    M64 = np.zeros((dk, dv))
+    for t in range(64):
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0.8, 1.0, dk)
+        b = rng.uniform(0.2, 0.9)
+        k, q, v, a = (x.astype(np.float32).astype(np.float64) for x in (k, q, v, a))
+        b = float(np.float32(b))
+        o32 = ora.step_f32(M32, q, k, v, a, b, True)
+        o64 = ora.step_f64(M64, q, k, v, a, b, True)
+        assert np.max(np.abs(o32 - o64)) <= 1e-5 * max(1.0, np.max(np.abs(o64)))
+
+
+# ------------------------------------------------------------ Proposition 1
+
+@pytest.mark.parametrize("gate_vec", [False, True])
+def test_prop1_misaligned_error_decays_by_gates_only(ora, gate_vec):
+    """Error in rows orthogonal to every key is only scaled by the gates:
+    E_T = diag(prod a) E_0 (the state update is linear in M)."""
+    rng = np.random.default_rng(7)
+    dk, dv, T = 16, 12, 20
+    M = rng.standard_normal((dk, dv))
+    E0 = np.zeros((dk, dv))
+    E0[12:] = rng.standard_normal((4, dv))      # rows 12..15
+    Me = M + E0
+    gprod = np.ones(dk)
+    for t in range(T):
+        k = np.zeros(dk); k[:12] = rng.standard_normal(12); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0.8, 1.0, dk if gate_vec else 1)
+        beta = rng.uniform(0.1, 1.0)
+        ora.step_f64(M, q, k, v, a, beta, gate_vec)
+        ora.step_f64(Me, q, k, v, a, beta, gate_vec)
+        gprod *= a if gate_vec else a[0]
+    np.testing.assert_allclose(Me - M, gprod[:, None] * E0, atol=1e-12, rtol=0)
+
+
+def test_prop1_aligned_error_removed(ora):
+    """Error aligned with the incoming key (E = k e^T) is scaled by
+    a(1 - beta |k|^2): removed for beta = 1, kept otherwise."""
+    rng = np.random.default_rng(8)
+    dk, dv = 16, 8
+    for beta in (1.0, 0.3):
+        M = rng.standard_normal((dk, dv))
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        e = rng.standard_normal(dv)
+        Me = M + np.outer(k, e)
+        q, v = rng.standard_normal(dk), rng.standard_normal(dv)
+        a = np.array([0.9])
+        ora.step_f64(M, q, k, v, a, beta, False)
+        ora.step_f64(Me, q, k, v, a, beta, False)
+        np.testing.assert_allclose(Me - M, 0.9 * (1 - beta) * np.outer(k, e), atol=1e-12)
+
+
+# ------------------------------------------------------ storage and quantizer
+
+def _random_head(rng, widths, dv, rf16=True):
+    dk = len(widths)
+    n = np.zeros((dk, dv), np.int64)
+    hv = np.zeros((dk, dv), np.uint16)
+    for i, b in enumerate(int(x) for x in widths):
+        if b == 16:
+            hv[i] = rng.standard_normal(dv).astype(np.float16).view(np.uint16)
+        else:
+            qm = (1 << (b - 1)) - 1
+            n[i] = rng.integers(-qm, qm + 1, dv)
+    r = rng.uniform(0.01, 2.0, dk)
+    r = r.astype(np.float16).astype(np.float32) if rf16 else r.astype(np.float32)
+    r[np.asarray(widths) == 16] = 0
+    c = rng.uniform(0.05, 3.0, dv).astype(np.float16).astype(np.float32)
+    return n, hv, r, c
+
+
+@pytest.mark.parametrize("keyrow", [False, True])
+def test_unpack_reads_the_stated_format(ora, keyrow):
+    """A head written by the test's own bit packer must dequantize to
+    RN(n r c) (exact product in fp64, then one rounding) and pivots to their
+    fp16 values: pins bit order, offset-binary codes and section offsets."""
+    rng = np.random.default_rng(9)
+    dk, dv, H = 16, 16, 3
+    if keyrow:
+        bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), H * dk)
+    else:
+        bits = np.array([4, 6, 8], np.uint8)
+    cfg = _cfg(ora, H=H, dk=dk, dv=dv, keyrow=keyrow, bits=bits)
+    slot = cfg.new_slot()
+    for h in range(H):
+        widths = bits[h * dk:(h + 1) * dk] if keyrow else np.full(dk, bits[h])
+        n, hv, r, c = _random_head(rng, widths, dv)
+        lay = cfg.head_layout(h)
+        slotcodec.write_head(slot, lay, widths, n, hv, r, c, True, True)
+        M = cfg.unpack_head(slot, h)
+        want = (n * r[:, None].astype(np.float64) * c[None, :].astype(np.float64)).astype(np.float32)
+        piv = widths == 16
+        want[piv] = hv[piv].view(np.float16).astype(np.float32)
+        assert np.array_equal(M, want)
+
+
+@pytest.mark.parametrize("width", [4, 6, 8])
+def test_pack_matches_bruteforce_quantizer(ora, width):
+    """For the scales the oracle fits, each code is the nearest level
+    argmin_n |M - n r c| except where M/(r c) sits within 1e-5 of a half level;
+    no error exceeds half a step; every row reaches +-qmax (normal fp16 scales);
+    every column's scale bounds its largest entry."""
+    rng = np.random.default_rng(10 + width)
+    dk = dv = 32
+    cfg = _cfg(ora, dk=dk, dv=dv, width=width)
+    qm = (1 << (width - 1)) - 1
+    for trial in range(10):
+        M = (rng.standard_normal((dk, dv)) * rng.uniform(0.1, 3, dk)[:, None]
+             * rng.uniform(0.1, 3, dv)[None, :]).astype(np.float32)
+        slot = cfg.new_slot()
+        cfg.pack_head(slot, 0, M)
+        n, _, r, c = slotcodec.read_head(slot, cfg.head_layout(0), np.full(dk, width), dk, dv, True, True)
+        step = r[:, None].astype(np.float64) * c[None, :]
+        x = M / step
+        levels = np.arange(-qm, qm + 1)
+        brute = levels[np.argmin(np.abs(x[..., None] - levels), axis=-1)]
+        near_half = np.abs(np.abs(x - np.floor(x)) - 0.5) < 1e-5
+        assert np.all((n == brute) | near_half)
+        assert np.all(np.abs(M - n * step) <= 0.5 * step * (1 + 1e-5))
+        assert np.all(np.abs(n).max(axis=1) == qm)
+        assert np.all(c >= np.abs(M).max(axis=0) * (1 - 2 ** -10))
+
+
+@pytest.mark.parametrize("width", [4, 6, 8])
+def test_requantize_of_dequantize_is_idempotent(ora, width):
+    """pack(unpack(Q)) keeps every code; scales move by at most 2 fp16 ulp."""
+    rng = np.random.default_rng(20 + width)
+    dk = dv = 32
+    cfg = _cfg(ora, dk=dk, dv=dv, width=width)
+    for trial in range(10):
+        M = rng.standard_normal((dk, dv)).astype(np.float32)
+        s1 = cfg.new_slot()
+        cfg.pack_head(s1, 0, M)
+        s2 = cfg.new_slot()
+        cfg.pack_head(s2, 0, cfg.unpack_head(s1, 0))
+        lay = cfg.head_layout(0)
+        n1, _, r1, c1 = slotcodec.read_head(s1, lay, np.full(dk, width), dk, dv, True, True)
+        n2, _, r2, c2 = slotcodec.read_head(s2, lay, np.full(dk, width), dk, dv, True, True)
+        assert np.array_equal(n1, n2)
+        ulp = lambda x: np.abs(x.astype(np.float16).view(np.int16).astype(np.int64))
+        assert np.max(np.abs(ulp(r1) - ulp(r2))) <= 2
+        assert np.max(np.abs(ulp(c1) - ulp(c2))) <= 2
+
+
+def test_pivot_rows_do_not_set_column_scales(ora):
+    """FP16 pivot key rows are stored raw, so their (here 100x larger) entries
+    must not widen the column scales of the quantized rows."""
+    rng = np.random.default_rng(11)
+    dk = dv = 16
+    bits = np.full(dk, 8, np.uint8)
+    bits[[2, 9]] = 16
+    cfg = _cfg(ora, dk=dk, dv=dv, keyrow=True, bits=bits)
+    M = rng.standard_normal((dk, dv)).astype(np.float32)
+    M[[2, 9]] *= 100
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, M)
+    n, hv, r, c = slotcodec.read_head(slot, cfg.head_layout(0), bits, dk, dv, True, True)
+    cmax = np.abs(np.delete(M, [2, 9], axis=0)).max(axis=0)
+    assert np.all(np.abs(c / cmax - 1) <= 2 ** -11)
+    assert np.array_equal(hv[[2, 9]], M[[2, 9]].astype(np.float16).view(np.uint16))
+    assert np.all(r[[2, 9]] == 0)
+
+
+def test_zero_state_gives_zero_codes_and_scales(ora):
+    cfg = _cfg(ora, dk=16, dv=16, width=4)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, np.zeros((16, 16), np.float32))
+    n, _, r, c = slotcodec.read_head(slot, cfg.head_layout(0), np.full(16, 4), 16, 16, True, True)
+    assert np.all(n == 0) and np.all(r == 0) and np.all(c == 0)
+
+
+def test_fp16_scale_saturates(ora):
+    """Entries beyond the fp16 range give a finite column scale of 65504."""
+    cfg = _cfg(ora, dk=8, dv=8, width=8)
+    M = np.ones((8, 8), np.float32)
+    M[0, 0] = 1e6
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, M)
+    _, _, _, c = slotcodec.read_head(slot, cfg.head_layout(0), np.full(8, 8), 8, 8, True, True)
+    assert c[0] == 65504.0 and np.all(np.isfinite(c))
+
+
+# --------------------------------------------------------- storage accounting
+
+def test_storage_accounting_matches_pages(ora):
+    """6-bit STEPQuant with fp16 row+column scales at d=128 and 1.39% FP16 pivot
+    heads compresses the fp32 state about 5.03x (essay); the layout must land
+    within 1% of that (appendix D with the exact format is not on the pages)."""
+    g = json.load(open(GOLDEN))
+    H = 72  # 1 pivot head of 72 = 1.39%
+    bits = np.full(H, 6, np.uint8)
+    bits[0] = 16
+    assert abs(1 / H - g["pivot_head_fraction_qwen"]["value"]) < 1e-4
+    cfg = _cfg(ora, H=H, dk=128, dv=128, bits=bits)
+    ratio = H * 128 * 128 * 4 / cfg.slot_bytes
+    assert abs(ratio / g["compression_6bit_qwen"]["value"] - 1) < 0.01
+    # KDA: 6-bit key rows, about 1% pivot rows
+    Hk = 32
+    kb = np.full(Hk * 128, 6, np.uint8)
+    kb[np.arange(0, Hk * 128, 100)] = 16
+    cfgk = _cfg(ora, H=Hk, dk=128, dv=128, keyrow=True, bits=kb)
+    rk = Hk * 128 * 128 * 4 / cfgk.slot_bytes
+    assert abs(rk / g["compression_6bit_kimi"]["value"] - 1) < 0.02
+
+
+def test_serving_pool_size(ora):
+    """B=512, H=32, d=128, 31 four-bit heads and one fp16 pivot head, four
+    layers: 4 x 512 x (31 x (8192+256+256) + 32768) bytes, against fp32."""
+    w = synth.WORKLOADS["serving_gdn"]
+    cfg = ora.Cfg.from_workload(w, synth.unit_bits(w))
+    assert cfg.slot_bytes == 31 * 8704 + 32768
+    pool = w.layers * w.B * cfg.slot_bytes
+    fp32 = w.layers * w.B * w.H * 128 * 128 * 4
+    assert abs(pool / 1e9 - 0.62) < 0.01 and abs(fp32 / 1e9 - 4.29) < 0.01
+
+
+# --------------------------------------------------- quantized vs unquantized
+
+@pytest.mark.parametrize("width,tol", [(16, 2e-3), (8, 3e-2)])
+def test_quantized_step_tracks_fp64(ora, width, tol):
+    """Every-step requantization at 8 bits (and fp16 pivots) stays close to the
+    exact recurrence over 32 steps: catches misplaced scales or gates."""
+    rng = np.random.default_rng(30 + width)
+    dk = dv = 32
+    for gate_vec in (False, True):
+        cfg = _cfg(ora, dk=dk, dv=dv, keyrow=gate_vec, gate_vec=gate_vec, width=width)
+        slot = cfg.new_slot()
+        M = np.zeros((dk, dv))
+        for t in range(32):
+            k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+            q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+            v = rng.standard_normal(dv)
+            a = rng.uniform(0.85, 1.0, dk if gate_vec else 1)
+            b = rng.uniform(0.3, 1.0)
+            k, q, v, a = (x.astype(np.float32) for x in (k, q, v, a))
+            o = cfg.step_head(slot, 0, q, k, v, a, b)
+            o64 = ora.step_f64(M, q, k, v, a, float(np.float32(b)), gate_vec)
+            assert np.max(np.abs(o - o64)) <= tol * np.max(np.abs(o64))
+
+
+def test_all_pivot_is_fp16_recurrence(ora):
+    """All units FP16 pivots: the state after each step is the fp16 rounding of
+    the fp32 step applied to the previous fp16 state (numpy half casts)."""
+    rng = np.random.default_rng(40)
+    dk = dv = 16
+    cfg = _cfg(ora, dk=dk, dv=dv, width=16)
+    slot = cfg.new_slot()
+    M = np.zeros((dk, dv), np.float32)
+    for t in range(10):
+        k = rng.standard_normal(dk).astype(np.float32)
+        q = rng.standard_normal(dk).astype(np.float32)
+        v = rng.standard_normal(dv).astype(np.float32)
+        a = np.float32(rng.uniform(0.8, 1.0))
+        cfg.step_head(slot, 0, q, k, v, a, 0.5)
+        ora.step_f32(M, q, k, v, np.array([a]), 0.5, False)
+        M = M.astype(np.float16).astype(np.float32)
+        assert np.array_equal(cfg.unpack_head(slot, 0), M)
+
+
+# ------------------------------------------------------------ windowed mode
+
+def _window_cfg(ora, W=4, K=5, dk=16, dv=16):
+    return _cfg(ora, dk=dk, dv=dv, keyrow=True, gate_vec=True, width=8, window=W, comps=K)
+
+
+def test_window_pack_selects_topk_by_bruteforce(ora):
+    """Compensation entries are the K largest |M| (ties to the lower index),
+    stored in index order with their exact fp32 values; the rest is quantized
+    with those positions at code 0."""
+    rng = np.random.default_rng(50)
+    W, K = 4, 7
+    cfg = _window_cfg(ora, W, K)
+    M = rng.standard_normal((16, 16)).astype(np.float32)
+    M[3, 4] = M[9, 1] = -5.0          # a tie in magnitude
+    M.flat[200] = 5.0
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, M)
+    lay = cfg.head_layout(0)
+    idx = slot[lay["cidx"]:lay["cidx"] + 2 * K].view(np.uint16)
+    val = slot[lay["cval"]:lay["cval"] + 4 * K].view(np.float32)
+    flat = M.reshape(-1)
+    order = np.lexsort((np.arange(flat.size), -np.abs(flat)))
+    want = np.sort(order[:K])
+    assert np.array_equal(idx, want)
+    assert np.array_equal(val, flat[want])
+    n, _, r, c = slotcodec.read_head(slot, lay, np.full(16, 8), 16, 16, True, True)
+    assert np.all(n.reshape(-1)[want] == 0)
+    rest = np.ones(flat.size, bool); rest[want] = False
+    assert np.all(c >= np.where(rest.reshape(16, 16), np.abs(M), 0).max(axis=0) * (1 - 2 ** -10))
+    back = cfg.unpack_head(slot, 0).reshape(-1)
+    assert np.array_equal(back[want], flat[want])
+
+
+def test_window_topk_ties_at_the_cut(ora):
+    """Many equal magnitudes across the K-th place: the lower linear indices win."""
+    W, K = 4, 6
+    cfg = _window_cfg(ora, W, K)
+    M = np.zeros((16, 16), np.float32)
+    tied = [17, 40, 41, 90, 130, 200, 201, 250]     # eight entries of |3|
+    for t, x in enumerate(tied):
+        M.flat[x] = 3.0 if t % 2 else -3.0
+    M.flat[5] = 7.0
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, M)
+    lay = cfg.head_layout(0)
+    idx = slot[lay["cidx"]:lay["cidx"] + 2 * K].view(np.uint16)
+    assert idx.tolist() == sorted([5] + tied[:5])
+
+
+def test_window_in_window_matches_dense_recurrence(ora):
+    """Inside a window the outputs come from the fixed base plus fp32 deltas:
+    they match the exact recurrence started from the dequantized base, and
+    the materialized state before the window end matches it too."""
+    rng = np.random.default_rng(51)
+    W, K, dk, dv = 6, 4, 16, 16
+    cfg = _window_cfg(ora, W, K, dk, dv)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, rng.standard_normal((dk, dv)).astype(np.float32))
+    M = cfg.unpack_head(slot, 0).astype(np.float64)
+    for t in range(W - 1):
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0.8, 1.0, dk)
+        k, q, v, a = (x.astype(np.float32) for x in (k, q, v, a))
+        o = cfg.step_head(slot, 0, q, k, v, a, 0.7)
+        o64 = ora.step_f64(M, q, k, v, a, float(np.float32(0.7)), True)
+        np.testing.assert_allclose(o, o64, atol=2e-5 * np.abs(o64).max(), rtol=0)
+        np.testing.assert_allclose(cfg.unpack_head(slot, 0), M, atol=2e-5 * np.abs(M).max(), rtol=0)
+    # the W-th step closes the window: deltas cleared, gates reset
+    k = np.eye(dk, dtype=np.float32)[0]
+    cfg.step_head(slot, 0, k, k, np.zeros(dv, np.float32), np.ones(dk, np.float32), 0.5)
+    lay = cfg.head_layout(0)
+    assert slot[lay["wn"]:lay["wn"] + 4].view(np.int32)[0] == 0
+    assert np.all(slot[lay["g"]:lay["g"] + 4 * dk].view(np.float32) == 1.0)
+
+
+def test_window_one_tracks_per_step(ora):
+    """W = 1 is not allowed to drift from every-step requantization: outputs of
+    the two modes (different rounding order) agree to 1e-5 relative."""
+    rng = np.random.default_rng(52)
+    dk = dv = 16
+    per = _cfg(ora, dk=dk, dv=dv, keyrow=True, gate_vec=True, width=8)
+    win = _cfg(ora, dk=dk, dv=dv, keyrow=True, gate_vec=True, width=8, window=2, comps=0)
+    s1, s2 = per.new_slot(), win.new_slot()
+    for t in range(2):
+        k = rng.standard_normal(dk).astype(np.float32)
+        q = rng.standard_normal(dk).astype(np.float32)
+        v = rng.standard_normal(dv).astype(np.float32)
+        a = rng.uniform(0.8, 1, dk).astype(np.float32)
+        o1 = per.step_head(s1, 0, q, k, v, a, 0.5)
+        o2 = win.step_head(s2, 0, q, k, v, a, 0.5)
+        if t == 0:
+            np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-5 * np.abs(o1).max())
+
+
+# ------------------------------------------------------------- workloads
+
+def test_workload_metadata():
+    w = synth.WORKLOADS["qwen_gdn"]
+    b = synth.unit_bits(w)
+    assert sorted(np.unique(b, return_counts=True)[1].tolist()) == [1, 10, 10, 11]
+    assert np.mean(b[b != 16]) == 6.0
+    k = synth.unit_bits(synth.WORKLOADS["kimi_kda"])
+    assert (k == 16).sum() == 41 and set(np.unique(k)) == {4, 16}
+    s = synth.unit_bits(synth.WORKLOADS["serving_gdn"])
+    assert (s == 16).sum() == 1 and (s == 4).sum() == 31
+
+
+def test_inputs_regenerate_per_unit():
+    w = synth.WORKLOADS["kimi_kda"].with_(B=8)
+    full = synth.batch_inputs(w, 0, 3)
+    one = synth.step_inputs(w, 0, 3, 5, 7)
+    assert np.array_equal(full.q[5, 7], one.q) and np.array_equal(full.a[5, 7], one.a)
+    assert np.all((one.a > 0.8) & (one.a < 1.0))
+    assert abs(np.linalg.norm(one.k) - 1) < 1e-2
+    M0 = synth.initial_state(w, 0, 2, 3)
+    med = np.median(np.abs(M0))
+    big = np.abs(M0) > 5 * med
+    assert 5 <= big.any(axis=1).sum() <= 128 and big.sum() < 0.2 * M0.size
