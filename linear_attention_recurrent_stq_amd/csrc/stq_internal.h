@@ -1,0 +1,62 @@
+// Internal definitions shared by the host side (stq_host.cpp) and the gfx950
+// kernels (stq_kernels.hip).  Not part of the ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace stq {
+
+// Per-head entry of the device layout table (in the pool header).  Offsets
+// are in bytes from the start of the head's region inside a slot.
+struct HeadDesc {
+    uint32_t off;      // region offset inside the slot
+    uint32_t bytes;    // region size
+    uint32_t rs;       // row scales (valid if nquant > 0)
+    uint32_t cs;       // column scales (valid if nquant > 0 and column scales on)
+    uint32_t wn;       // windowed: delta count (int32)
+    uint32_t g;        // windowed: cumulative gate [d_k] fp32
+    uint32_t cidx;     // windowed: compensation index [K] uint16
+    uint32_t cval;     // windowed: compensation value [K] fp32
+    uint32_t du;       // windowed: delta values [W][d_v] fp32
+    uint32_t dkap;     // windowed: delta keys [W][d_k] fp32
+    uint32_t rows;     // first entry of this head in the row table
+    uint16_t width;    // width shared by every row (4/6/8/16), 0 if rows differ
+    uint16_t nquant;   // number of quantized (non-pivot) rows
+    uint32_t pad[4];
+};
+static_assert(sizeof(HeadDesc) == 64, "HeadDesc is 64 bytes");
+
+// Row table entry: (byte offset of the row inside the head region) << 5 | width.
+__host__ __device__ inline uint32_t row_entry(uint32_t off, uint32_t width) { return (off << 5) | width; }
+__host__ __device__ inline uint32_t row_off(uint32_t e) { return e >> 5; }
+__host__ __device__ inline uint32_t row_width(uint32_t e) { return e & 31u; }
+
+// Kernel arguments (passed by value).
+struct Args {
+    uint8_t *slots;              // first slot (pool base + header bytes)
+    const HeadDesc *heads;       // [H]
+    const uint32_t *rows;        // [H * d_k]
+    uint64_t slot_bytes;
+    const int32_t *slot_ids;     // [B]
+    const void *q, *k, *v;       // [B,H,d] io dtype
+    const float *a;              // [B,H] or [B,H,d_k]
+    const float *beta;           // [B,H]
+    float *o;                    // [B,H,d_v]
+    float *state;                // pack / unpack: [B,H,d_k,d_v]
+    int32_t B, H, nslots;
+    int32_t io_bf16, gate_vec, rs16, cs16;
+    int32_t window, comps;
+};
+
+// Launchers (stq_kernels.hip).  Return the launch's hipError_t.
+hipError_t launch_step(const Args &a, int dk, int dv, hipStream_t s);
+hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s);
+hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s);
+hipError_t launch_pool_init(uint8_t *slots, uint64_t slot_bytes, int32_t nslots,
+                            const HeadDesc *heads, int32_t H, int32_t dk, int32_t window,
+                            hipStream_t s);
+
+}  // namespace stq

@@ -1,0 +1,120 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function declared in include/stq.h, computes the same slot layout as the
+oracle, and rejects bad arguments before launching anything."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def stq():
+    import linear_attention_recurrent_stq_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(stq):
+    hdr = open(os.path.join(ROOT, "include", "stq.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(stq_\w+)\s*\(", hdr, re.M))
+    assert {"stq_pack_layout", "stq_alloc_pool", "stq_decode_step", "stq_unpack"} <= declared
+    lib = stq.library()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert set(stq.SYMBOLS) == declared
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_layout_matches_oracle(stq, ora, name):
+    w = synth.WORKLOADS[name]
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    o = ora.Cfg.from_workload(w, bits)
+    assert L.slot_bytes == o.slot_bytes
+    for h in range(w.H):
+        off, nb = L.head(h)
+        lay = o.head_layout(h)
+        assert (off, nb) == (lay["base"], lay["bytes"])
+
+
+def test_layout_mixed_rows_matches_oracle(stq, ora):
+    rng = np.random.default_rng(0)
+    for d in (64, 128):
+        bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), 5 * d)
+        L = stq.Layout(5, d, d, bits, unit=stq.UNIT_KEYROW, gate=stq.GATE_KEYVEC, window=8, comps=20)
+        o = ora.Cfg(5, d, d, True, True, True, True, 8, 20, bits)
+        assert L.slot_bytes == o.slot_bytes
+        for h in range(5):
+            assert L.head(h) == (o.head_layout(h)["base"], o.head_layout(h)["bytes"])
+
+
+def test_pool_size_query_without_device(stq):
+    w = synth.WORKLOADS["serving_gdn"]
+    L = stq.Layout.from_workload(w, synth.unit_bits(w))
+    q = stq.StqPool()
+    assert stq.library().stq_alloc_pool(L.handle, 512, None, 0, None, C.byref(q)) == stq.STQ_OK
+    assert q.bytes == L.header_bytes + 512 * 302592
+    assert L.header_bytes % 256 == 0 and L.header_bytes >= 64 * 32 + 4 * 32 * 128
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("H", 0, 1), ("d_k", 96, 2), ("d_v", 32, 2), ("unit", 5, 1), ("gate", 2, 1),
+    ("row_scale", 0, 1), ("col_scale", 1, 1), ("io_dtype", 2, 1), ("window", 0, 1),
+    ("window", 65, 2), ("comps", 3, 1), ("comps", -1, 1),
+])
+def test_config_rejected(stq, field, value, status):
+    bits = np.full(4, 4, np.uint8)
+    cfg = stq.StqConfig(4, 64, 64, 0, 0, stq.F16, stq.F16, stq.BF16, 1, 0,
+                        bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+    setattr(cfg, field, value)
+    h = C.c_void_p()
+    assert stq.library().stq_pack_layout(C.byref(cfg), C.byref(h)) == status
+    assert not h.value
+    assert stq.library().stq_last_error().decode()
+
+
+def test_bad_widths_and_too_many_comps(stq):
+    with pytest.raises(stq.StqError) as e:
+        stq.Layout(2, 64, 64, np.array([4, 5], np.uint8))
+    assert "unit_bits[1]" in str(e.value)
+    with pytest.raises(stq.StqError):
+        # a head of pivot rows only leaves no entry for compensation
+        bits = np.full(2 * 64, 16, np.uint8)
+        stq.Layout(2, 64, 64, bits, unit=stq.UNIT_KEYROW, window=4, comps=1)
+    with pytest.raises(stq.StqError):
+        stq.Layout(2, 64, 64, np.array([4, 4], np.uint8), window=1, comps=2)
+
+
+def test_calls_validate_before_launch(stq):
+    lib = stq.library()
+    w = synth.WORKLOADS["tiny_gdn"]
+    L = stq.Layout.from_workload(w, synth.unit_bits(w))
+    pool = stq.StqPool()
+    assert lib.stq_decode_step(C.byref(pool), 1, None, None, None, None, None, None, None, None) \
+        == stq.STQ_ERR_INVALID
+    fake = stq.StqPool(C.c_void_p(0x100000), 1 << 20, 4, L.handle)
+    P = C.c_void_p
+    assert lib.stq_decode_step(C.byref(fake), -1, P(16), P(16), P(16), P(16), P(16), P(16), P(16), None) \
+        == stq.STQ_ERR_INVALID
+    assert lib.stq_decode_step(C.byref(fake), 5, P(16), P(16), P(16), P(16), P(16), P(16), P(16), None) \
+        == stq.STQ_ERR_INVALID  # B > slots
+    assert lib.stq_decode_step(C.byref(fake), 2, P(16), P(24), P(16), P(16), P(16), P(16), P(16), None) \
+        == stq.STQ_ERR_ALIGN
+    assert lib.stq_decode_step(C.byref(fake), 2, P(18), P(16), P(16), P(16), P(16), P(16), P(16), None) \
+        == stq.STQ_ERR_ALIGN
+    assert lib.stq_decode_step(C.byref(fake), 2, P(16), None, P(16), P(16), P(16), P(16), P(16), None) \
+        == stq.STQ_ERR_INVALID
+    assert lib.stq_decode_step(C.byref(fake), 0, None, None, None, None, None, None, None, None) \
+        == stq.STQ_OK
+    assert lib.stq_unpack(C.byref(fake), 2, P(16), None, None) == stq.STQ_ERR_INVALID
+    assert lib.stq_pack(C.byref(fake), 2, P(16), P(8), None) == stq.STQ_ERR_ALIGN
+    small = C.c_size_t(0)
+    out = stq.StqPool()
+    assert lib.stq_alloc_pool(L.handle, 4, P(0x100000), 100, None, C.byref(out)) == stq.STQ_ERR_TOO_SMALL
+    assert lib.stq_alloc_pool(L.handle, 4, P(0x100008), 1 << 20, None, C.byref(out)) == stq.STQ_ERR_ALIGN
+    assert lib.stq_layout_head(L.handle, 7, C.byref(small), None) == stq.STQ_ERR_INVALID

@@ -1,0 +1,204 @@
+"""HIP path vs the CPU oracle through the C ABI, on seeded inputs.
+
+Bar: slot bytes (codes, scales, pivots) identical to the oracle's, and every
+output vector within max relative error 1e-4 (the arithmetic is specified to
+the rounding, so both are expected to be exact; the bar is what is asserted).
+"""
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-4
+
+
+def _harness(*a, **k):
+    from tests.parity import Harness
+    return Harness(*a, **k)
+
+
+def _check_step(o_gpu, o_ref, follow, t, tag):
+    from tests.parity import rel_err
+    worst = 0.0
+    for n, (b, h) in enumerate(follow):
+        e = rel_err(o_gpu[b, h], o_ref[n])
+        worst = max(worst, e)
+        assert e <= O_TOL, f"{tag}: o mismatch at step {t}, unit (b={b}, h={h}): rel err {e:.3g}"
+    return worst
+
+
+def _run(w, T, follow=None, bits=None, check_slots_every=0, tag=""):
+    print(f"[{tag}] {w.name} B={w.B} H={w.H} d={w.dk} T={T}", flush=True)
+    hs = _harness(w, follow=follow, bits=bits)
+    try:
+        hs.init_state()
+        if w.init != "zero":
+            bad = hs.compare_slots()
+            assert not bad, f"{tag}: packed initial state differs: {bad[:4]}"
+        for t in range(T):
+            if follow is None:
+                x = hs.load_full(t)
+                o_gpu, o_ref = hs.step(x)
+            else:
+                x = hs.load_followed(t)
+                o_gpu, o_ref = hs.step(x, idx_in_x=True)
+            _check_step(o_gpu, o_ref, hs.follow, t, tag)
+            if check_slots_every and (t + 1) % check_slots_every == 0:
+                bad = hs.compare_slots()
+                assert not bad, f"{tag}: slot bytes differ after step {t}: {bad[:4]}"
+        bad = hs.compare_slots()
+        assert not bad, f"{tag}: slot bytes differ after {T} steps: {bad[:4]}"
+        return hs
+    finally:
+        hs.close()
+
+
+def test_tiny_gdn_every_step():
+    """B=4, H=2, d=64, uniform 6-bit, fp32 row scales, fp32 io: all units, all 16 steps."""
+    _run(synth.WORKLOADS["tiny_gdn"], 16, check_slots_every=1, tag="tiny")
+
+
+def test_qwen_gdn_mixed_widths_small_batch():
+    """Per-head 4/6/8-bit and an FP16 pivot head, bf16 io, B=8, 24 steps, all units."""
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=8)
+    _run(w, 24, check_slots_every=8, tag="qwen-small")
+
+
+def test_kimi_kda_outliers_small_batch():
+    """Per-key-row widths (4-bit + FP16 pivot rows), vector gate, outlier start."""
+    w = synth.WORKLOADS["kimi_kda"].with_(B=4)
+    _run(w, 24, check_slots_every=8, tag="kimi-small")
+
+
+def test_mixed_row_widths_d64():
+    """KDA rows of every width {4,6,8,16} in one state, d=64: the per-row path."""
+    w = synth.WORKLOADS["kimi_kda"].with_(B=3, H=4, dk=64, dv=64, name="kda_mixed_d64")
+    rng = np.random.default_rng(0)
+    bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), w.H * w.dk, p=[0.4, 0.25, 0.25, 0.1])
+    _run(w, 20, bits=bits, check_slots_every=5, tag="kda-mixed")
+
+
+def test_qwen_gdn_full_batch_sampled_units():
+    """Full B=64 x H=32 batch on the GPU, 48 followed units over all 256 steps."""
+    w = synth.WORKLOADS["qwen_gdn"]
+    rng = np.random.default_rng(2)
+    follow = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 48), rng.integers(0, w.H, 48))})
+    hs = _harness(w, follow=follow)
+    try:
+        hs.load_full(0)  # every unit gets real inputs once; followed units get theirs each step
+        for t in range(w.T):
+            x = hs.load_followed(t)
+            o_gpu, o_ref = hs.step(x, idx_in_x=True)
+            _check_step(o_gpu, o_ref, hs.follow, t, "qwen-full")
+        assert not hs.compare_slots()
+    finally:
+        hs.close()
+
+
+def test_serving_gdn_all_units_short():
+    """B=512 x H=32 (16,384 states, 31 four-bit heads + 1 pivot head): all units, 3 steps."""
+    _run(synth.WORKLOADS["serving_gdn"], 3, tag="serving-all")
+
+
+def test_kimi_kda_full_batch_all_units():
+    """B=256 x H=32 KDA with outlier start: every unit for 2 steps after the pack."""
+    _run(synth.WORKLOADS["kimi_kda"], 2, tag="kimi-all")
+
+
+def test_unpack_and_pack_match_oracle():
+    """stq_unpack equals the oracle's dequantization; stq_pack of a random fp32
+    state gives the oracle's bytes (mixed widths, pivots, outliers)."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["kimi_kda"].with_(B=4)
+    hs = _harness(w)
+    try:
+        hs.init_state()
+        for t in range(3):
+            hs.step(hs.load_full(t))
+        got = hs.unpack_gpu()
+        for b, h in hs.follow:
+            want = hs.ocfg.unpack_head(hs.oslots[b], h)
+            assert np.array_equal(got[b, h], want), (b, h)
+        rng = np.random.default_rng(3)
+        M = (rng.standard_normal((w.B, w.H, w.dk, w.dv)) * 0.3).astype(np.float32)
+        stq.pack(hs.pool, hs.slot_ids, torch.from_numpy(M).cuda())
+        for b, h in hs.follow:
+            hs.ocfg.pack_head(hs.oslots[b], h, M[b, h])
+        assert not hs.compare_slots()
+    finally:
+        hs.close()
+
+
+def test_invalid_slot_id_touches_nothing():
+    """An out-of-range slot id yields a NaN output and leaves every slot unchanged."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=4)
+    hs = _harness(w)
+    try:
+        hs.load_full(0)
+        hs.step(hs.load_full(0))
+        before = hs.slot_bytes_gpu()
+        ids = hs.slot_ids.clone()
+        ids[2] = 1000
+        stq.decode_step(hs.pool, ids, hs.q, hs.k, hs.v, hs.a, hs.beta, hs.o)
+        torch.cuda.synchronize()
+        o = hs.o.cpu().numpy()
+        assert np.isnan(o[2]).all() and np.isfinite(o[[0, 1, 3]]).all()
+        after = hs.slot_bytes_gpu()
+        assert np.array_equal(before[hs.slot_of[2]], after[hs.slot_of[2]])
+        assert np.array_equal(before[np.setdiff1d(np.arange(4), hs.slot_of[[0, 1, 3]])],
+                              after[np.setdiff1d(np.arange(4), hs.slot_of[[0, 1, 3]])])
+    finally:
+        hs.close()
+
+
+def test_deterministic_and_batch_independent():
+    """Same inputs twice give identical bytes; a request's result does not
+    depend on which other requests share the call (B=1 vs B=5)."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=5)
+    outs = []
+    for rep in range(2):
+        hs = _harness(w)
+        try:
+            for t in range(4):
+                hs.step(hs.load_full(t))
+            outs.append(hs.slot_bytes_gpu())
+            if rep == 1:
+                # replay request 3 alone into a fresh 1-slot pool
+                L = hs.L
+                p1 = stq.Pool(L, 1)
+                ids = torch.zeros(1, dtype=torch.int32, device="cuda")
+                o1 = torch.empty(1, w.H, w.dv, device="cuda")
+                for t in range(4):
+                    x = synth.batch_inputs(w, 0, t)
+                    q, k, v = (hs._to_dev(x))
+                    stq.decode_step(p1, ids, q[3:4].cuda().contiguous(), k[3:4].cuda().contiguous(),
+                                    v[3:4].cuda().contiguous(), torch.from_numpy(x.a[3:4]).cuda(),
+                                    torch.from_numpy(x.beta[3:4]).cuda(), o1)
+                alone = p1.slots_view().cpu().numpy()[0]
+                assert np.array_equal(alone, outs[1][hs.slot_of[3]])
+        finally:
+            hs.close()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_empty_batch_is_a_noop():
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["tiny_gdn"]
+    hs = _harness(w)
+    try:
+        before = hs.slot_bytes_gpu()
+        e = torch.empty(0, dtype=torch.int32, device="cuda")
+        z = lambda *s, dt=torch.float32: torch.empty(*s, dtype=dt, device="cuda")
+        stq.decode_step(hs.pool, e, z(0, 2, 64), z(0, 2, 64), z(0, 2, 64), z(0, 2), z(0, 2), z(0, 2, 64))
+        torch.cuda.synchronize()
+        assert np.array_equal(before, hs.slot_bytes_gpu())
+    finally:
+        hs.close()
