@@ -59,15 +59,19 @@
  * compensation positions: their fp32 value), cumulative gate g (1 at a
  * window start), deltas (u_m, kap_m), m = 1..n:
  *   kap_m,i = RN(kap_m,i*a_i);  g_i = RN(g_i*a_i)
- *   w_j = csum(B_.j, RN(g*k));  w_j = fma(u_m,j, csum(kap_m, k), w_j), m = 1..n
+ *   w_j = csum(Bq_.j, RN(g*k)), Bq = B without its compensation entries;
+ *         then each compensation entry (i, j, val) of column j, in index
+ *         order: w_j = fma(val, RN(g_i*k_i), w_j)  (a compensation entry is a
+ *         token with a one-hot key on the ordinary update path);
+ *         then w_j = fma(u_m,j, csum(kap_m, k), w_j), m = 1..n
  *   u_j = RN(beta*RN(v_j - w_j));  append (u, kap = k)
- *   o_j = csum(B_.j, RN(g*q));  o_j = fma(u_m,j, csum(kap_m, q), o_j), m = 1..n+1
+ *   o_j: the same with q in place of k, over m = 1..n+1
  *   at n+1 == W:  D_ij = RN(kap_1,i*u_1,j), D_ij = fma(kap_m,i, u_m,j, D_ij)
  *                 for m = 2..W;  M_ij = fma(g_i, B_ij, D_ij);  the K entries of
- *                 largest |M_ij| among non-pivot rows (ties: lower i*d_v+j)
- *                 become compensation values, the rest is requantized as above
- *                 with those positions left out of both maxima (code 0);
- *                 g = 1, n = 0.
+ *                 largest |M_ij| among non-pivot rows (ties: lower index
+ *                 p = j*d_k + i, column-major) become compensation values,
+ *                 stored by ascending p; the rest is requantized as above with
+ *                 those positions left out of both maxima (code 0); g = 1, n = 0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -357,16 +361,20 @@ static void unit_write(const ora_cfg *c, int h, uint8_t *slot, const ora_unit *u
     }
 }
 
-/* Base dequantization B_ij = RN(n_ij * r_i * c_j) (n*r is exact), pivots and comps. */
-static void dequant_base(const ora_cfg *c, const ora_unit *u, float *B) {
+/* Base dequantization B_ij = RN(n_ij * r_i * c_j) (n*r is exact) and pivots;
+ * with_comps: compensation entries overwrite their positions. */
+static void dequant_base(const ora_cfg *c, const ora_unit *u, float *B, int with_comps) {
     for (int i = 0; i < c->dk; ++i)
         for (int j = 0; j < c->dv; ++j) {
             size_t e = (size_t)i * c->dv + j;
             if (u->bw[i] == 16) B[e] = f16_val(u->hv[e]);
             else B[e] = ((float)u->n[e] * u->r[i]) * u->c[j];
         }
-    if (c->window > 1)
-        for (int t = 0; t < c->comps; ++t) B[u->cidx[t]] = u->cval[t];
+    if (c->window > 1 && with_comps)
+        for (int t = 0; t < c->comps; ++t) {
+            int i = u->cidx[t] % c->dk, j = u->cidx[t] / c->dk;
+            B[(size_t)i * c->dv + j] = u->cval[t];
+        }
 }
 
 /* Requantize M into u (codes, pivots, scales).  skip[e] != 0 excludes an entry. */
@@ -421,7 +429,8 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
     free(Z);
 }
 
-/* Top-K |M| among entries of non-pivot rows; ties to the lower linear index. */
+/* Top-K |M| among entries of non-pivot rows; ties to the lower column-major
+ * index p = j*dk + i.  Stored by ascending p. */
 typedef struct { float mag; uint32_t idx; } ora_ent;
 static int ent_cmp(const void *pa, const void *pb) {
     const ora_ent *a = pa, *b = pb;
@@ -439,9 +448,8 @@ static void select_comps(const ora_cfg *c, ora_unit *u, const float *M, uint8_t 
     for (int i = 0; i < c->dk; ++i) {
         if (u->bw[i] == 16) continue;
         for (int j = 0; j < c->dv; ++j) {
-            size_t x = (size_t)i * c->dv + j;
-            all[m].mag = fabsf(M[x]);
-            all[m].idx = (uint32_t)x;
+            all[m].mag = fabsf(M[(size_t)i * c->dv + j]);
+            all[m].idx = (uint32_t)((size_t)j * c->dk + i);
             ++m;
         }
     }
@@ -450,8 +458,9 @@ static void select_comps(const ora_cfg *c, ora_unit *u, const float *M, uint8_t 
     for (int t = 0; t < c->comps; ++t) u->cidx[t] = (uint16_t)all[t].idx;
     qsort(u->cidx, (size_t)c->comps, sizeof(uint16_t), idx_cmp);
     for (int t = 0; t < c->comps; ++t) {
-        u->cval[t] = M[u->cidx[t]];
-        skip[u->cidx[t]] = 1;
+        size_t x = (size_t)(u->cidx[t] % c->dk) * c->dv + u->cidx[t] / c->dk;
+        u->cval[t] = M[x];
+        skip[x] = 1;
     }
     free(all);
 }
@@ -475,7 +484,7 @@ void ora_unpack_head(const ora_cfg *c, int h, const uint8_t *slot, float *M) {
     ora_unit u;
     unit_alloc(c, &u);
     unit_read(c, h, slot, &u);
-    dequant_base(c, &u, M);
+    dequant_base(c, &u, M, 1);
     if (c->window > 1 && u.nd > 0) {
         for (int i = 0; i < c->dk; ++i)
             for (int j = 0; j < c->dv; ++j) {
@@ -552,7 +561,9 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
         float *ck = malloc(sizeof(float) * (size_t)(W + 1));
         float *cq = malloc(sizeof(float) * (size_t)(W + 1));
         float *un = malloc(sizeof(float) * (size_t)dv);
-        dequant_base(c, &u, B);
+        float *Bc = malloc(sizeof(float) * e);
+        dequant_base(c, &u, B, 0);
+        dequant_base(c, &u, Bc, 1);
         for (int m = 0; m < n; ++m)
             for (int i = 0; i < dk; ++i) u.dkap[(size_t)m * dk + i] *= ai[i];
         for (int i = 0; i < dk; ++i) {
@@ -563,6 +574,8 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
         for (int m = 0; m < n; ++m) ck[m] = csum(u.dkap + (size_t)m * dk, 1, k, dk);
         for (int j = 0; j < dv; ++j) {
             float w = csum(B + j, (size_t)dv, kg, dk);
+            for (int t = 0; t < c->comps; ++t)
+                if (u.cidx[t] / dk == j) w = fmaf(u.cval[t], kg[u.cidx[t] % dk], w);
             for (int m = 0; m < n; ++m) w = fmaf(u.du[(size_t)m * dv + j], ck[m], w);
             un[j] = beta * (v[j] - w);
         }
@@ -572,6 +585,8 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
         for (int m = 0; m < n; ++m) cq[m] = csum(u.dkap + (size_t)m * dk, 1, q, dk);
         for (int j = 0; j < dv; ++j) {
             float p = csum(B + j, (size_t)dv, qg, dk);
+            for (int t = 0; t < c->comps; ++t)
+                if (u.cidx[t] / dk == j) p = fmaf(u.cval[t], qg[u.cidx[t] % dk], p);
             for (int m = 0; m < n; ++m) p = fmaf(u.du[(size_t)m * dv + j], cq[m], p);
             o[j] = p;
         }
@@ -583,7 +598,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
                     float D = u.dkap[i] * u.du[j];
                     for (int m = 1; m < W; ++m)
                         D = fmaf(u.dkap[(size_t)m * dk + i], u.du[(size_t)m * dv + j], D);
-                    M[x] = fmaf(u.g[i], B[x], D);
+                    M[x] = fmaf(u.g[i], Bc[x], D);
                 }
             uint8_t *skip = calloc(e, 1);
             select_comps(c, &u, M, skip);
@@ -594,7 +609,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
             memset(u.dkap, 0, sizeof(float) * (size_t)W * dk);
             free(skip);
         }
-        free(B); free(kg); free(qg); free(ck); free(cq); free(un);
+        free(B); free(Bc); free(kg); free(qg); free(ck); free(cq); free(un);
     }
     unit_write(c, h, slot, &u);
     free(M);

@@ -410,9 +410,9 @@ def _window_cfg(ora, W=4, K=5, dk=16, dv=16):
 
 
 def test_window_pack_selects_topk_by_bruteforce(ora):
-    """Compensation entries are the K largest |M| (ties to the lower index),
-    stored in index order with their exact fp32 values; the rest is quantized
-    with those positions at code 0."""
+    """Compensation entries are the K largest |M| (ties to the lower
+    column-major index j*d_k + i), stored in index order with their exact fp32
+    values; the rest is quantized with those positions at code 0."""
     rng = np.random.default_rng(50)
     W, K = 4, 7
     cfg = _window_cfg(ora, W, K)
@@ -424,28 +424,29 @@ def test_window_pack_selects_topk_by_bruteforce(ora):
     lay = cfg.head_layout(0)
     idx = slot[lay["cidx"]:lay["cidx"] + 2 * K].view(np.uint16)
     val = slot[lay["cval"]:lay["cval"] + 4 * K].view(np.float32)
-    flat = M.reshape(-1)
+    flat = M.T.reshape(-1)                     # column-major: p = j*16 + i
     order = np.lexsort((np.arange(flat.size), -np.abs(flat)))
     want = np.sort(order[:K])
     assert np.array_equal(idx, want)
     assert np.array_equal(val, flat[want])
     n, _, r, c = slotcodec.read_head(slot, lay, np.full(16, 8), 16, 16, True, True)
-    assert np.all(n.reshape(-1)[want] == 0)
+    assert np.all(n.T.reshape(-1)[want] == 0)
     rest = np.ones(flat.size, bool); rest[want] = False
-    assert np.all(c >= np.where(rest.reshape(16, 16), np.abs(M), 0).max(axis=0) * (1 - 2 ** -10))
-    back = cfg.unpack_head(slot, 0).reshape(-1)
+    assert np.all(c >= np.where(rest.reshape(16, 16).T, np.abs(M), 0).max(axis=0) * (1 - 2 ** -10))
+    back = cfg.unpack_head(slot, 0).T.reshape(-1)
     assert np.array_equal(back[want], flat[want])
 
 
 def test_window_topk_ties_at_the_cut(ora):
-    """Many equal magnitudes across the K-th place: the lower linear indices win."""
+    """Many equal magnitudes across the K-th place: the lower column-major
+    indices j*d_k + i win."""
     W, K = 4, 6
     cfg = _window_cfg(ora, W, K)
     M = np.zeros((16, 16), np.float32)
-    tied = [17, 40, 41, 90, 130, 200, 201, 250]     # eight entries of |3|
-    for t, x in enumerate(tied):
-        M.flat[x] = 3.0 if t % 2 else -3.0
-    M.flat[5] = 7.0
+    tied = [17, 40, 41, 90, 130, 200, 201, 250]     # eight entries of |3|, by p
+    for t, p in enumerate(tied):
+        M[p % 16, p // 16] = 3.0 if t % 2 else -3.0
+    M[5, 0] = 7.0
     slot = cfg.new_slot()
     cfg.pack_head(slot, 0, M)
     lay = cfg.head_layout(0)
