@@ -18,6 +18,7 @@
 
 struct stq_layout {
     stq_config cfg;                     // unit_bits cleared; widths live in `bits`
+    bool mixed = false;                 // some head has rows of different widths
     std::vector<uint8_t> bits;          // H or H*d_k unit widths
     std::vector<stq::HeadDesc> heads;   // [H]
     std::vector<uint32_t> rows;         // [H*d_k] row table
@@ -159,6 +160,8 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
         }
         d.width = (uint16_t)common;
         d.nquant = (uint16_t)nq;
+        if (common == 0) L->mixed = true;
+        d.cbytes = (uint32_t)p;
         p = up(p, 16);
         if (nq > 0) {
             d.rs = (uint32_t)p;
@@ -263,7 +266,7 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
     a.a = d_a;
     a.beta = d_beta;
     a.o = d_o;
-    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, static_cast<hipStream_t>(stream)),
+    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->mixed, static_cast<hipStream_t>(stream)),
                     "decode step");
 }
 

@@ -25,7 +25,8 @@ struct HeadDesc {
     uint32_t rows;     // first entry of this head in the row table
     uint16_t width;    // width shared by every row (4/6/8/16), 0 if rows differ
     uint16_t nquant;   // number of quantized (non-pivot) rows
-    uint32_t pad[4];
+    uint32_t cbytes;   // bytes of the code rows (a multiple of 16)
+    uint32_t pad[3];
 };
 static_assert(sizeof(HeadDesc) == 64, "HeadDesc is 64 bytes");
 
@@ -51,8 +52,9 @@ struct Args {
     int32_t window, comps;
 };
 
-// Launchers (stq_kernels.hip).  Return the launch's hipError_t.
-hipError_t launch_step(const Args &a, int dk, int dv, hipStream_t s);
+// Launchers (stq_kernels.hip).  Return the launch's hipError_t.  `mixed`: some
+// head of the layout has rows of different widths.
+hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s);
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_pool_init(uint8_t *slots, uint64_t slot_bytes, int32_t nslots,

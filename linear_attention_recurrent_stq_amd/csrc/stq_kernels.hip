@@ -19,7 +19,9 @@
 //   w_j = csum_i(A_ij k_i);  u_j = RN(beta RN(v_j - w_j))
 //   M_ij = fma(k_i, u_j, A_ij);  o_j = csum_i(M_ij q_i)
 //   c'_j = H(max_i |M_ij|);  Z_ij = RN(M_ij RN(1/c'_j))
-//   r'_i = H(RN(max_j |Z_ij| / qmax_i));  n'_ij = clamp(rne(Z_ij RN(1/r'_i)))
+//   r'_i = Hup(RN(max_j |Z_ij| / qmax_i)) (smallest fp16 not below; fp32 row
+//   scales: RN);  n'_ij = rne(Z_ij RN(1/r'_i)) -- rounding the step up keeps
+//   |n'| <= qmax, so the clamp is applied only to a row whose step saturated.
 // csum: blocks of 8 rows as fma chains from RN(x0 y0), block sums left to right.
 // Codes are offset binary (u = n + 2^(b-1)) in LSB-first row bit streams.
 #include <hip/hip_fp16.h>
@@ -42,22 +44,17 @@ __device__ __forceinline__ float f16v(uint32_t bits) {
     return __half2float(__ushort_as_half((unsigned short)(bits & 0xffffu)));
 }
 
-// 8 consecutive io values (bf16 or fp32) starting at element e (e % 8 == 0).
-__device__ __forceinline__ void load8(const void *p, int bf16, size_t e, float out[8]) {
-    if (bf16) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + e);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            out[2 * c] = __uint_as_float(w[c] << 16);
-            out[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
-        }
-    } else {
-        const float4 *f = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + e);
-        const float4 a = f[0], b = f[1];
-        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-    }
+// Hup(x), x >= 0: the smallest fp16 not below x, saturating at 65504.
+__device__ __forceinline__ uint32_t h16up(float x) {
+    uint32_t h = h16(x);
+    if (f16v(h) < x && h != 0x7bffu) ++h;
+    return h;
+}
+
+// Hides a value from the optimizer so byte extractions stay v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
 }
 
 __device__ __forceinline__ float load1(const void *p, int bf16, size_t e) {
@@ -98,19 +95,22 @@ __device__ __forceinline__ void store_piece(uint8_t *row, int cg, int w, uint4 r
     }
 }
 
-// Unsigned (offset-binary) codes of a piece as floats.
+// Unsigned (offset-binary) codes of a piece as floats.  For 4-bit pieces the
+// odd codes come out multiplied by 16 (their nibble stays in place); the
+// caller scales them by g/16, which is exact.
 __device__ __forceinline__ void codes_f(uint4 r, int w, float u[8]) {
     if (w == 4) {
-        const uint32_t lo = r.x & 0x0F0F0F0Fu, hi = (r.x >> 4) & 0x0F0F0F0Fu;
+        const uint32_t lo = opaque(r.x & 0x0F0F0F0Fu), hi = opaque(r.x & 0xF0F0F0F0u);
         u[0] = (float)(lo & 0xffu);         u[1] = (float)(hi & 0xffu);
         u[2] = (float)((lo >> 8) & 0xffu);  u[3] = (float)((hi >> 8) & 0xffu);
         u[4] = (float)((lo >> 16) & 0xffu); u[5] = (float)((hi >> 16) & 0xffu);
         u[6] = (float)(lo >> 24);           u[7] = (float)(hi >> 24);
     } else if (w == 8) {
-        u[0] = (float)(r.x & 0xffu);         u[1] = (float)((r.x >> 8) & 0xffu);
-        u[2] = (float)((r.x >> 16) & 0xffu); u[3] = (float)(r.x >> 24);
-        u[4] = (float)(r.y & 0xffu);         u[5] = (float)((r.y >> 8) & 0xffu);
-        u[6] = (float)((r.y >> 16) & 0xffu); u[7] = (float)(r.y >> 24);
+        const uint32_t x = opaque(r.x), y = opaque(r.y);
+        u[0] = (float)(x & 0xffu);         u[1] = (float)((x >> 8) & 0xffu);
+        u[2] = (float)((x >> 16) & 0xffu); u[3] = (float)(x >> 24);
+        u[4] = (float)(y & 0xffu);         u[5] = (float)((y >> 8) & 0xffu);
+        u[6] = (float)((y >> 16) & 0xffu); u[7] = (float)(y >> 24);
     } else {  // 6
         const uint64_t v = (uint64_t)r.x | ((uint64_t)r.y << 32);
 #pragma unroll
@@ -118,34 +118,106 @@ __device__ __forceinline__ void codes_f(uint4 r, int w, float u[8]) {
     }
 }
 
-// Pack 8 quantized values y (kMagic + 2^(w-1) + n, clamped) into a piece.
+// Codes scaled by the row step: RN((u - 2^(w-1)) * g), with u, g and the
+// offset term exact, so one fma rounds once.  g16 = g / 16, nog = -2^(w-1) g.
+__device__ __forceinline__ void dequant_row(uint4 raw, int w, float g, float g16, float nog, float x[8]) {
+    float u[8];
+    codes_f(raw, w, u);
+    if (w == 4) {
+#pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+            x[c] = fma_(u[c], g, nog);
+            x[c + 1] = fma_(u[c + 1], g16, nog);
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = fma_(u[c], g, nog);
+    }
+}
+
+// Pack 8 quantized values y = 1.5*2^23 + 2^(w-1) + n into a piece: the low
+// byte of each pattern is the offset-binary code (no carry out of the field).
 __device__ __forceinline__ uint4 pack_codes(const float y[8], int w) {
     uint4 r = make_uint4(0, 0, 0, 0);
-    uint32_t u[8];
+    uint32_t b[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) u[c] = __float_as_uint(y[c]) & ((1u << w) - 1u);
+    for (int c = 0; c < 8; ++c) b[c] = __float_as_uint(y[c]);
     if (w == 4) {
-        r.x = u[0] | (u[1] << 4) | (u[2] << 8) | (u[3] << 12) | (u[4] << 16) | (u[5] << 20) |
-              (u[6] << 24) | (u[7] << 28);
+        // byte 0 of each pair word = two nibbles, byte 1 = 0
+        const uint32_t p01 = (b[1] << 4) | b[0], p23 = (b[3] << 4) | b[2];
+        const uint32_t p45 = (b[5] << 4) | b[4], p67 = (b[7] << 4) | b[6];
+        r.x = __builtin_amdgcn_perm(p23, p01, 0x0c0c0400u) | __builtin_amdgcn_perm(p67, p45, 0x04000c0cu);
     } else if (w == 8) {
-        r.x = u[0] | (u[1] << 8) | (u[2] << 16) | (u[3] << 24);
-        r.y = u[4] | (u[5] << 8) | (u[6] << 16) | (u[7] << 24);
+        // byte 1 of each pattern is 0, so a shifted or keeps two clean bytes
+        const uint32_t p01 = (b[1] << 8) | b[0], p23 = (b[3] << 8) | b[2];
+        const uint32_t p45 = (b[5] << 8) | b[4], p67 = (b[7] << 8) | b[6];
+        r.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        r.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
     } else {  // 6
+        uint32_t u[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) u[c] = b[c] & 63u;
         r.x = u[0] | (u[1] << 6) | (u[2] << 12) | (u[3] << 18) | (u[4] << 24) | (u[5] << 30);
         r.y = (u[5] >> 2) | (u[6] << 4) | (u[7] << 10);
     }
     return r;
 }
 
+// LDS of one workgroup.  The per-thread partials are stored element-major,
+// thread-minor ([c][t], with t = rg * d_v/8 + cg): each write of the 64 lanes of
+// a wave is then one contiguous run, and the 4-float pad spreads the combining
+// reads (a column's partials sit at [j % 8][rg * d_v/8 + j / 8]; a row's at
+// [i % 8][i / 8 * d_v/8 + cg]) over the banks.
 template <int DK, int DV>
 struct Lds {
-    float colp[DK / 8][DV];  // column partial sums
-    float colm[DK / 8][DV];  // column partial maxima
-    float rowm[DV / 8][DK];  // row partial maxima
-    float u[DV];
-    float ic[DV];
-    float ir[DK];
+    static constexpr int NT = DK * DV / 64;
+    static constexpr int NTP = NT + 4;
+    float colp[8][NTP];         // column partial sums: [c][t]
+    union {
+        float colm[8][NTP];     // column partial maxima: [c][t]
+        float rowm[8][NTP];     // row partial maxima: [r][t] (after the column maxima are used)
+    };
+    float g[DK];                // per key row: gated row step RN(a r)
+    float g16[DK];              //   g / 16
+    float nog[DK];              //   -2^(w-1) g
+    float af[DK];               //   gate
+    float kf[DK], qf[DK];       //   k and q as fp32
+    float cf[DV];               // column scales (1 when absent)
+    float u[DV];                // u = beta (v - w)
+    float ic[DV];               // 1 / c'
+    float ir[DK];               // 1 / r'; negated when the row step saturated
 };
+
+// Left-to-right sum of the d_k/8 block partials of column j.
+template <int DK, int DV>
+__device__ __forceinline__ float col_sum(const Lds<DK, DV> &sm, int j) {
+    constexpr int CG = DV / 8, RG = DK / 8;
+    const float *p = &sm.colp[j & 7][j >> 3];
+    float s = p[0];
+#pragma unroll
+    for (int g = 1; g < RG; ++g) s = s + p[g * CG];
+    return s;
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ float col_max(const Lds<DK, DV> &sm, int j) {
+    constexpr int CG = DV / 8, RG = DK / 8;
+    const float *p = &sm.colm[j & 7][j >> 3];
+    float m = p[0];
+#pragma unroll
+    for (int g = 1; g < RG; ++g) m = fmaxf(m, p[g * CG]);
+    return m;
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ float row_max(const Lds<DK, DV> &sm, int i) {
+    constexpr int CG = DV / 8;
+    const float *p = &sm.rowm[i & 7][(i >> 3) * CG];
+    float m = p[0];
+#pragma unroll
+    for (int g = 1; g < CG; ++g) m = fmaxf(m, p[g]);
+    return m;
+}
 
 // Per-thread view of one state during a step / pack.
 struct Rows {
@@ -174,6 +246,43 @@ __device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i
     return W ? W : (int)row_width(A.rows[hd.rows + i]);
 }
 
+// Whether the head has quantized rows: known from the width unless rows differ.
+template <int W>
+__device__ __forceinline__ bool has_quant(const HeadDesc &hd) {
+    return W == 16 ? false : (W != 0 ? true : hd.nquant > 0);
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read8(const float *p, float (&out)[N], int o) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0];
+    const float4 b = reinterpret_cast<const float4 *>(p)[1];
+    out[o + 0] = a.x; out[o + 1] = a.y; out[o + 2] = a.z; out[o + 3] = a.w;
+    out[o + 4] = b.x; out[o + 5] = b.y; out[o + 6] = b.z; out[o + 7] = b.w;
+}
+
+__device__ __forceinline__ uint4 pivot_piece(const float (&x)[8]) {
+    uint4 p;
+    p.x = h16(x[0]) | (h16(x[1]) << 16);
+    p.y = h16(x[2]) | (h16(x[3]) << 16);
+    p.z = h16(x[4]) | (h16(x[5]) << 16);
+    p.w = h16(x[6]) | (h16(x[7]) << 16);
+    return p;
+}
+
+// Quantize one row of 8 values with 1/r' = ir and store the piece.
+template <bool CLAMP>
+__device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir, const float (&x)[8]) {
+    const float off = (float)(1 << (w - 1));
+    const float mg = kMagic + off;
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        y[c] = fma_(x[c], ir, mg);
+        if (CLAMP) y[c] = fminf(fmaxf(y[c], mg - (off - 1.0f)), mg + (off - 1.0f));
+    }
+    store_piece(row, cg, w, pack_codes(y, w));
+}
+
 // Column scales, row scales, codes and pivots of x (the thread's 8x8 block of
 // the fp32 state) written back into the head region R.  If emit_o, the column
 // partial sums of o are already in sm.colp and o is combined and stored in the
@@ -182,8 +291,7 @@ template <int DK, int DV, int W>
 __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd, uint8_t *R,
                                               const Rows &rw, float (&x)[8][8], Lds<DK, DV> &sm,
                                               int t, int rg, int cg, bool emit_o, size_t unit) {
-    constexpr int RG = DK / 8, CG = DV / 8;
-    const bool quant = hd.nquant > 0;
+    const bool quant = has_quant<W>(hd);
     const bool cs = quant && A.cs16;
     // column maxima over quantized rows
     if (cs) {
@@ -193,22 +301,15 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 if (rw.w[r] != 16) m = fmaxf(m, fabsf(x[r][c]));
-            sm.colm[rg][8 * cg + c] = m;
+            sm.colm[c][t] = m;
         }
     }
     if (cs || emit_o) __syncthreads();
     if (t < DV) {
-        if (emit_o) {
-            float o = sm.colp[0][t];
-#pragma unroll
-            for (int g = 1; g < RG; ++g) o = o + sm.colp[g][t];
-            A.o[unit * DV + t] = o;
-        }
+        if (emit_o) A.o[unit * DV + t] = col_sum<DK, DV>(sm, t);
         float ic = 1.0f;
         if (cs) {
-            float C = sm.colm[0][t];
-#pragma unroll
-            for (int g = 1; g < RG; ++g) C = fmaxf(C, sm.colm[g][t]);
+            const float C = col_max<DK, DV>(sm, t);
             const uint32_t hc = h16(C);
             const float cv = f16v(hc);
             ic = cv > 0.0f ? 1.0f / cv : 0.0f;
@@ -219,20 +320,12 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
     if (!quant) {
         // all rows are FP16 pivots: store and finish
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            uint4 p;
-            p.x = h16(x[r][0]) | (h16(x[r][1]) << 16);
-            p.y = h16(x[r][2]) | (h16(x[r][3]) << 16);
-            p.z = h16(x[r][4]) | (h16(x[r][5]) << 16);
-            p.w = h16(x[r][6]) | (h16(x[r][7]) << 16);
-            store_piece(R + rw.ro[r], cg, 16, p);
-        }
+        for (int r = 0; r < 8; ++r) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
         return;
     }
     __syncthreads();
     float icc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) icc[c] = sm.ic[8 * cg + c];
+    lds_read8(&sm.ic[8 * cg], icc, 0);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         float m = 0.0f;
@@ -244,109 +337,111 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
                 m = fmaxf(m, fabsf(z));
             }
         }
-        sm.rowm[cg][8 * rg + r] = m;
+        sm.rowm[r][t] = m;
     }
     __syncthreads();
     if (t < DK) {
         const int w = width_of<W>(A, hd, t);
-        float ir = 0.0f;
-        float rv = 0.0f;
+        float ir = 0.0f, rv = 0.0f;
+        bool sat = false;
         if (w != 16) {
-            float Rm = sm.rowm[0][t];
-#pragma unroll
-            for (int g = 1; g < CG; ++g) Rm = fmaxf(Rm, sm.rowm[g][t]);
+            const float Rm = row_max<DK, DV>(sm, t);
             const float rq = Rm / (float)((1 << (w - 1)) - 1);
-            rv = A.rs16 ? f16v(h16(rq)) : rq;
+            if (A.rs16) {
+                rv = f16v(h16up(rq));
+                sat = rq > 65504.0f;
+            } else {
+                rv = rq;
+            }
             ir = rv > 0.0f ? 1.0f / rv : 0.0f;
+            if (__builtin_isinf(ir)) ir = 0.0f;
         }
         if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)h16(rv);
         else reinterpret_cast<float *>(R + hd.rs)[t] = rv;
-        sm.ir[t] = ir;
+        sm.ir[t] = sat ? -ir : ir;
     }
     __syncthreads();
+    float irr[8];
+    lds_read8(&sm.ir[8 * rg], irr, 0);
+    bool anysat = false;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int w = rw.w[r];
-        uint4 p;
-        if (w == 16) {
-            p.x = h16(x[r][0]) | (h16(x[r][1]) << 16);
-            p.y = h16(x[r][2]) | (h16(x[r][3]) << 16);
-            p.z = h16(x[r][4]) | (h16(x[r][5]) << 16);
-            p.w = h16(x[r][6]) | (h16(x[r][7]) << 16);
-        } else {
-            const float irr = sm.ir[8 * rg + r];
-            const float off = (float)(1 << (w - 1));
-            const float mg = kMagic + off;
-            const float lo = mg - (off - 1.0f), hi = mg + (off - 1.0f);
-            float y[8];
+    for (int r = 0; r < 8; ++r) anysat |= irr[r] < 0.0f;
+    if (__builtin_expect(__any(anysat), 0)) {
+        // a row step saturated at 65504: clamp codes to +-qmax
 #pragma unroll
-            for (int c = 0; c < 8; ++c) y[c] = fminf(fmaxf(fma_(x[r][c], irr, mg), lo), hi);
-            p = pack_codes(y, w);
+        for (int r = 0; r < 8; ++r) {
+            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
+            else quant_row<true>(R + rw.ro[r], cg, rw.w[r], fabsf(irr[r]), x[r]);
         }
-        store_piece(R + rw.ro[r], cg, w, p);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
+            else quant_row<false>(R + rw.ro[r], cg, rw.w[r], irr[r], x[r]);
+        }
     }
 }
 
 // ----------------------------------------------------------------- step
 
 template <int DK, int DV, int W>
-__device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uint8_t *R,
-                                          Lds<DK, DV> &sm, int t, int rg, int cg, size_t unit,
-                                          const float (&kk)[8], const float (&qq)[8],
-                                          const float (&aa)[8], float beta, float vv) {
-    constexpr int RG = DK / 8;
+__device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
+                                          Lds<DK, DV> &sm, int t, int rg, int cg) {
+    const bool quant = has_quant<W>(hd);
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
     uint4 raw[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
-    float rr[8], cc[8];
-    const bool quant = hd.nquant > 0;
-    if (quant) {
-        if (A.rs16) {
-            const uint4 s = *reinterpret_cast<const uint4 *>(R + hd.rs + 16 * rg);
-            const uint32_t sv[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) { rr[2 * c] = f16v(sv[c]); rr[2 * c + 1] = f16v(sv[c] >> 16); }
-        } else {
-            const float4 *s = reinterpret_cast<const float4 *>(R + hd.rs + 32 * rg);
-            const float4 s0 = s[0], s1 = s[1];
-            rr[0] = s0.x; rr[1] = s0.y; rr[2] = s0.z; rr[3] = s0.w;
-            rr[4] = s1.x; rr[5] = s1.y; rr[6] = s1.z; rr[7] = s1.w;
-        }
-        if (A.cs16) {
-            const uint4 s = *reinterpret_cast<const uint4 *>(R + hd.cs + 16 * cg);
-            const uint32_t sv[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) { cc[2 * c] = f16v(sv[c]); cc[2 * c + 1] = f16v(sv[c] >> 16); }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) cc[c] = 1.0f;
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) { rr[c] = 0.0f; cc[c] = 1.0f; }
+
+    // per key row and per value column constants, computed once per state
+    const float beta = A.beta[unit];
+    float vv = 0.0f;
+    if (t < DK) {
+        const int i = t;
+        const int w = width_of<W>(A, hd, i);
+        const float a = A.gate_vec ? A.a[unit * DK + i] : A.a[unit];
+        float ri = 0.0f;
+        if (quant && w != 16)
+            ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
+                        : reinterpret_cast<const float *>(R + hd.rs)[i];
+        const float g = a * ri;
+        sm.g[i] = g;
+        sm.g16[i] = g * 0.0625f;
+        sm.nog[i] = w != 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
+        sm.af[i] = a;
+        sm.kf[i] = load1(A.k, A.io_bf16, unit * DK + i);
+        sm.qf[i] = load1(A.q, A.io_bf16, unit * DK + i);
     }
+    if (t < DV) {
+        sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+        vv = load1(A.v, A.io_bf16, unit * DV + t);
+    }
+    __syncthreads();
+
+    float kk[8], qq[8], cc[8];
+    lds_read8(&sm.kf[8 * rg], kk, 0);
+    lds_read8(&sm.qf[8 * rg], qq, 0);
+    lds_read8(&sm.cf[8 * cg], cc, 0);
 
     // decay + dequantize: A_ij
     float x[8][8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
+        const int i = 8 * rg + r;
         const int w = rw.w[r];
         if (w == 16) {
+            const float a = sm.af[i];
             const uint32_t hv[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                x[r][2 * c] = aa[r] * f16v(hv[c]);
-                x[r][2 * c + 1] = aa[r] * f16v(hv[c] >> 16);
+                x[r][2 * c] = a * f16v(hv[c]);
+                x[r][2 * c + 1] = a * f16v(hv[c] >> 16);
             }
         } else {
-            const float g = aa[r] * rr[r];
-            const float nog = -(float)(1 << (w - 1)) * g;
-            float u[8];
-            codes_f(raw[r], w, u);
+            dequant_row(raw[r], w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) x[r][c] = fma_(u[c], g, nog) * cc[c];
+            for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * cc[c];
         }
     }
 
@@ -356,19 +451,13 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         float s = x[0][c] * kk[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) s = fma_(x[r][c], kk[r], s);
-        sm.colp[rg][8 * cg + c] = s;
+        sm.colp[c][t] = s;
     }
     __syncthreads();
-    if (t < DV) {
-        float w = sm.colp[0][t];
-#pragma unroll
-        for (int g = 1; g < RG; ++g) w = w + sm.colp[g][t];
-        sm.u[t] = beta * (vv - w);
-    }
+    if (t < DV) sm.u[t] = beta * (vv - col_sum<DK, DV>(sm, t));
     __syncthreads();
     float uu[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) uu[c] = sm.u[8 * cg + c];
+    lds_read8(&sm.u[8 * cg], uu, 0);
 
     // rank-1 write and o = S_new q partial sums
 #pragma unroll
@@ -380,12 +469,15 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         float s = x[0][c] * qq[0];
 #pragma unroll
         for (int r = 1; r < 8; ++r) s = fma_(x[r][c], qq[r], s);
-        sm.colp[rg][8 * cg + c] = s;
+        sm.colp[c][t] = s;
     }
     requant_store<DK, DV, W>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
 }
 
-template <int DK, int DV>
+// One workgroup per (request, head) state.  MIXED: some head of the layout
+// has rows of different widths (KDA); without it the per-row width path is not
+// compiled, which saves registers.
+template <int DK, int DV, bool MIXED>
 __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
     constexpr int CG = DV / 8;
     __shared__ Lds<DK, DV> sm;
@@ -399,31 +491,16 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
         if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
         return;
     }
-    const HeadDesc hd = A.heads[h];
+    const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
-
-    float kk[8], qq[8], aa[8];
-    load8(A.k, A.io_bf16, unit * DK + 8 * rg, kk);
-    load8(A.q, A.io_bf16, unit * DK + 8 * rg, qq);
-    if (A.gate_vec) {
-        const float4 *p = reinterpret_cast<const float4 *>(A.a + unit * DK + 8 * rg);
-        const float4 a0 = p[0], a1 = p[1];
-        aa[0] = a0.x; aa[1] = a0.y; aa[2] = a0.z; aa[3] = a0.w;
-        aa[4] = a1.x; aa[5] = a1.y; aa[6] = a1.z; aa[7] = a1.w;
-    } else {
-        const float a = A.a[unit];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) aa[r] = a;
-    }
-    const float beta = A.beta[unit];
-    const float vv = t < DV ? load1(A.v, A.io_bf16, unit * DV + t) : 0.0f;
-
     switch (hd.width) {
-        case 4: step_tile<DK, DV, 4>(A, hd, R, sm, t, rg, cg, unit, kk, qq, aa, beta, vv); break;
-        case 6: step_tile<DK, DV, 6>(A, hd, R, sm, t, rg, cg, unit, kk, qq, aa, beta, vv); break;
-        case 8: step_tile<DK, DV, 8>(A, hd, R, sm, t, rg, cg, unit, kk, qq, aa, beta, vv); break;
-        case 16: step_tile<DK, DV, 16>(A, hd, R, sm, t, rg, cg, unit, kk, qq, aa, beta, vv); break;
-        default: step_tile<DK, DV, 0>(A, hd, R, sm, t, rg, cg, unit, kk, qq, aa, beta, vv); break;
+        case 4: step_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 6: step_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 8: step_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 16: step_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+        default:
+            if (MIXED) step_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            break;
     }
 }
 
@@ -502,15 +579,13 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack(Args A) {
             const float ri = !quant ? 0.0f
                              : A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
                                       : reinterpret_cast<const float *>(R + hd.rs)[i];
-            const float nor = -(float)(1 << (rw.w[r] - 1)) * ri;
-            float u[8];
-            codes_f(raw, rw.w[r], u);
+            dequant_row(raw, rw.w[r], ri, ri * 0.0625f, -(float)(1 << (rw.w[r] - 1)) * ri, x);
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float cj = (quant && A.cs16)
                                      ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[8 * cg + c])
                                      : 1.0f;
-                x[c] = fma_(u[c], ri, nor) * cj;
+                x[c] = x[c] * cj;
             }
         }
         float4 *p = reinterpret_cast<float4 *>(dst + (size_t)i * DV + 8 * cg);
@@ -555,7 +630,18 @@ hipError_t launch_dims(void (*k)(Args), const Args &a, hipStream_t s) {
     if (dk == 64 && dv == 128) return launch_dims<64, 128>(KERNEL<64, 128>, a, s);    \
     return hipErrorInvalidValue;
 
-hipError_t launch_step(const Args &a, int dk, int dv, hipStream_t s) { STQ_DISPATCH(k_step) }
+hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
+#define STQ_STEP(DK_, DV_)                                                                      \
+    if (dk == DK_ && dv == DV_)                                                                 \
+        return mixed ? launch_dims<DK_, DV_>(k_step<DK_, DV_, true>, a, s)                      \
+                     : launch_dims<DK_, DV_>(k_step<DK_, DV_, false>, a, s);
+    STQ_STEP(128, 128)
+    STQ_STEP(64, 64)
+    STQ_STEP(128, 64)
+    STQ_STEP(64, 128)
+#undef STQ_STEP
+    return hipErrorInvalidValue;
+}
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s) { STQ_DISPATCH(k_pack) }
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s) { STQ_DISPATCH(k_unpack) }
 

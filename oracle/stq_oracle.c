@@ -32,6 +32,7 @@
  *   RN(x)      fp32 round-to-nearest-even of the exact value.
  *   fma        one rounding of the exact a*b+c.
  *   H(x)       fp16 round-to-nearest-even after clamping to +-65504.
+ *   Hup(x)     smallest fp16 >= x (x >= 0), at most 65504.
  *   csum(x,y)  sum_i x_i*y_i over i = 0..d_k-1: blocks of 8 consecutive i,
  *              each s = RN(x0*y0) then s = fma(x_t, y_t, s); block sums are
  *              then added left to right with RN.
@@ -50,8 +51,11 @@
  *   column scale   C_j = max over non-pivot rows |M_ij|; c'_j = H(C_j);
  *                  ic_j = c'_j > 0 ? RN(1/c'_j) : 0;  Z_ij = RN(M_ij*ic_j)
  *                  (no column scale: Z = M)
- *   row scale      R_i = max_j |Z_ij|;  r'_i = H(RN(R_i/qmax_i))  (fp32 row
- *                  scale: r'_i = RN(R_i/qmax_i));  ir_i = r'_i > 0 ? RN(1/r'_i) : 0
+ *   row scale      R_i = max_j |Z_ij|;  r'_i = Hup(RN(R_i/qmax_i))  (fp32 row
+ *                  scale: r'_i = RN(R_i/qmax_i));  ir_i = RN(1/r'_i), or 0 when
+ *                  r'_i = 0 or 1/r'_i overflows.  Rounding the step up means
+ *                  |Z_ij*ir_i| < qmax + 1/2, so the clamp below only acts when
+ *                  the step saturated at 65504.
  *   codes          n'_ij = clamp(rne(Z_ij*ir_i exactly), -qmax_i, qmax_i)
  *                  pivot row: h'_ij = H(M_ij)
  *
@@ -71,7 +75,8 @@
  *                 largest |M_ij| among non-pivot rows (ties: lower index
  *                 p = j*d_k + i, column-major) become compensation values,
  *                 stored by ascending p; the rest is requantized as above with
- *                 those positions left out of both maxima (code 0); g = 1, n = 0.
+ *                 those positions left out of both maxima (code 0); g = 1, n = 0
+ *                 (delta storage is not cleared; pack clears it).
  */
 #include <math.h>
 #include <stdint.h>
@@ -207,6 +212,13 @@ static uint16_t H(float x) {
     if (x > 65504.0f) x = 65504.0f;
     if (x < -65504.0f) x = -65504.0f;
     return f16_bits(x);
+}
+
+/* Hup(x), x >= 0: the smallest fp16 not below x, saturating at 65504. */
+static uint16_t Hup(float x) {
+    uint16_t h = H(x);
+    if (f16_val(h) < x && h != 0x7bffu) ++h;   /* next fp16 up (positive patterns are ordered) */
+    return h;
 }
 
 void ora_f32_to_f16(const float *x, uint16_t *y, size_t n) {
@@ -413,8 +425,9 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
         }
         int qm = qmax_of(u->bw[i]);
         float rq = R / (float)qm;
-        u->r[i] = c->rscale_f16 ? f16_val(H(rq)) : rq;
+        u->r[i] = c->rscale_f16 ? f16_val(Hup(rq)) : rq;
         float ir = u->r[i] > 0.0f ? 1.0f / u->r[i] : 0.0f;
+        if (isinf(ir)) ir = 0.0f;
         for (int j = 0; j < dv; ++j) {
             size_t e = (size_t)i * dv + j;
             /* the product of two floats is exact in double; rint rounds ties to even */
@@ -604,9 +617,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
             select_comps(c, &u, M, skip);
             requantize(c, &u, M, skip);
             for (int i = 0; i < dk; ++i) u.g[i] = 1.0f;
-            u.nd = 0;
-            memset(u.du, 0, sizeof(float) * (size_t)W * dv);
-            memset(u.dkap, 0, sizeof(float) * (size_t)W * dk);
+            u.nd = 0;   /* the stored deltas are left as they are: only n counts */
             free(skip);
         }
         free(B); free(Bc); free(kg); free(qg); free(ck); free(cq); free(un);

@@ -307,6 +307,28 @@ def test_pivot_rows_do_not_set_column_scales(ora):
     assert np.all(r[[2, 9]] == 0)
 
 
+def test_row_step_rounds_up_and_never_clips(ora):
+    """The row step is the smallest fp16 not below absmax/qmax, so every
+    |M/(r c)| stays within qmax + 1/2 and no code clips (checked against
+    numpy's half rounding); this also pins the step to absmax/qmax."""
+    rng = np.random.default_rng(12)
+    dk = dv = 32
+    for width in (4, 6, 8):
+        qm = (1 << (width - 1)) - 1
+        cfg = _cfg(ora, dk=dk, dv=dv, width=width)
+        for trial in range(10):
+            M = (rng.standard_normal((dk, dv)) * rng.uniform(1e-3, 10, dk)[:, None]).astype(np.float32)
+            slot = cfg.new_slot()
+            cfg.pack_head(slot, 0, M)
+            n, _, r, c = slotcodec.read_head(slot, cfg.head_layout(0), np.full(dk, width), dk, dv, True, True)
+            Z = (M.astype(np.float64) / c[None, :].astype(np.float64))
+            need = np.abs(Z).max(axis=1) / qm
+            assert np.all(r >= need * (1 - 2 ** -22))                  # not below absmax/qmax
+            below = np.nextafter(r.astype(np.float16), np.float16(0)).astype(np.float64)
+            assert np.all((below < need * (1 + 2 ** -22)) | (r == 0))   # the smallest such fp16
+            assert np.all(np.abs(M / (r[:, None].astype(np.float64) * c[None, :])) <= qm + 0.5)
+
+
 def test_zero_state_gives_zero_codes_and_scales(ora):
     cfg = _cfg(ora, dk=16, dv=16, width=4)
     slot = cfg.new_slot()
