@@ -60,7 +60,7 @@ typedef struct {
     int32_t row_scale;       /* STQ_F16 | STQ_F32 */
     int32_t col_scale;       /* STQ_F16 | STQ_NONE */
     int32_t io_dtype;        /* q, k, v: STQ_BF16 | STQ_F32 (o is always fp32) */
-    int32_t window;          /* 1: requantize every step; 2..64: windowed */
+    int32_t window;          /* 1: requantize every step; 2..16: windowed */
     int32_t comps;           /* windowed: K fp32 compensation entries, 0..1024 */
     const uint8_t *unit_bits;/* host; H (per head) or H*d_k (per key row) widths
                                 in {4,6,8,16}; 16 = FP16 pivot unit */
@@ -80,7 +80,7 @@ const char *stq_last_error(void);
  * refitted online).  On success *out owns a new layout; free it with
  * stq_layout_free.  Errors: STQ_ERR_INVALID (NULL, H < 1, widths not in
  * {4,6,8,16}, bad enums, comps without window, comps > non-pivot entries),
- * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 64).
+ * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 16).
  */
 stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out);
 

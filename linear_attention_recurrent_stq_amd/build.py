@@ -8,8 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libstq.so")
-SOURCES = [os.path.join(HERE, "csrc", "stq_host.cpp"), os.path.join(HERE, "csrc", "stq_kernels.hip")]
-HEADERS = [os.path.join(ROOT, "include", "stq.h"), os.path.join(HERE, "csrc", "stq_internal.h")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("stq_host.cpp", "stq_kernels.hip", "stq_window.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

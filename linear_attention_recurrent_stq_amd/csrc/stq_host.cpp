@@ -55,7 +55,7 @@ stq_status check_cfg(const stq_config *c) {
     if (c->io_dtype != STQ_BF16 && c->io_dtype != STQ_F32)
         return fail(STQ_ERR_INVALID, "io_dtype must be STQ_BF16 or STQ_F32");
     if (c->window < 1) return fail(STQ_ERR_INVALID, "window must be >= 1");
-    if (c->window > 64) return fail(STQ_ERR_UNSUPPORTED, "window must be <= 64");
+    if (c->window > 16) return fail(STQ_ERR_UNSUPPORTED, "window must be <= 16");
     if (c->comps < 0 || c->comps > 1024) return fail(STQ_ERR_INVALID, "comps must be in [0, 1024]");
     if (c->window == 1 && c->comps != 0)
         return fail(STQ_ERR_INVALID, "compensation entries need the windowed mode (window > 1)");
@@ -258,7 +258,6 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
         if (!aligned(p, 16)) return fail(STQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
     }
     const stq_layout *L = pool->layout;
-    if (L->cfg.window > 1) return fail(STQ_ERR_UNSUPPORTED, "windowed decode is not built yet");
     stq::Args a = base_args(pool, B, d_slot_ids);
     a.q = d_q;
     a.k = d_k;
@@ -266,8 +265,10 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
     a.a = d_a;
     a.beta = d_beta;
     a.o = d_o;
-    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->mixed, static_cast<hipStream_t>(stream)),
-                    "decode step");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (L->cfg.window > 1)
+        return launched(stq::launch_step_win(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "windowed decode step");
+    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "decode step");
 }
 
 stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids, float *d_state,
@@ -278,11 +279,11 @@ stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids
     if (!d_state) return fail(STQ_ERR_INVALID, "state pointer is NULL");
     if (!aligned(d_state, 16)) return fail(STQ_ERR_ALIGN, "state must be 16-byte aligned");
     const stq_layout *L = pool->layout;
-    if (L->cfg.window > 1) return fail(STQ_ERR_UNSUPPORTED, "windowed unpack is not built yet");
     stq::Args a = base_args(pool, B, d_slot_ids);
     a.state = d_state;
-    return launched(stq::launch_unpack(a, L->cfg.d_k, L->cfg.d_v, static_cast<hipStream_t>(stream)),
-                    "unpack");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (L->cfg.window > 1) return launched(stq::launch_unpack_win(a, L->cfg.d_k, L->cfg.d_v, s), "unpack");
+    return launched(stq::launch_unpack(a, L->cfg.d_k, L->cfg.d_v, s), "unpack");
 }
 
 stq_status stq_pack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
@@ -293,11 +294,12 @@ stq_status stq_pack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
     if (!d_state) return fail(STQ_ERR_INVALID, "state pointer is NULL");
     if (!aligned(d_state, 16)) return fail(STQ_ERR_ALIGN, "state must be 16-byte aligned");
     const stq_layout *L = pool->layout;
-    if (L->cfg.window > 1) return fail(STQ_ERR_UNSUPPORTED, "windowed pack is not built yet");
     stq::Args a = base_args(pool, B, d_slot_ids);
     a.state = const_cast<float *>(d_state);
-    return launched(stq::launch_pack(a, L->cfg.d_k, L->cfg.d_v, static_cast<hipStream_t>(stream)),
-                    "pack");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (L->cfg.window > 1)
+        return launched(stq::launch_pack_win(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "pack");
+    return launched(stq::launch_pack(a, L->cfg.d_k, L->cfg.d_v, s), "pack");
 }
 
 }  // extern "C"

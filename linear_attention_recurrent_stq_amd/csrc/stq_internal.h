@@ -57,6 +57,10 @@ struct Args {
 hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s);
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s);
+// Windowed layouts (window > 1): stq_window.hip.
+hipError_t launch_step_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s);
+hipError_t launch_pack_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s);
+hipError_t launch_unpack_win(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_pool_init(uint8_t *slots, uint64_t slot_bytes, int32_t nslots,
                             const HeadDesc *heads, int32_t H, int32_t dk, int32_t window,
                             hipStream_t s);

@@ -1,386 +1,11 @@
-// HIP kernels for gfx950: decode step, pack, unpack and pool init of the
-// quantized recurrent state.
-//
-// One workgroup owns one (request, head) state of d_k x d_v.  Thread t holds an
-// 8 x 8 block: key rows 8*rg .. 8*rg+7 and value columns 8*cg .. 8*cg+7, with
-// rg = t / (d_v/8) and cg = t % (d_v/8) (256 threads at d = 128, one wave at
-// d = 64).  That block is the unit of every memory access: in a row of b-bit
-// codes the 8 codes of one thread are b contiguous bytes, so a row piece is one
-// 4 / 6 / 8 / 16-byte load.  Column sums are fma chains over the thread's 8
-// rows followed by a left-to-right sum of the d_k/8 block sums in LDS; column
-// and row maxima are combined the same way.  There is no matrix-core work:
-// every state element is touched once against one or two vectors, so the step
-// is a streaming mat-vec bound by HBM bandwidth and the VALU, not a GEMM.
-//
-// Arithmetic, per state (every rounding fixed so results are reproducible; the
-// pages state the method in words only: STEPQuant essay, background,
-// temporal-axis, spatial-axis and experiment-design paragraphs):
-//   g_i = RN(a_i r_i);  A_ij = RN(RN(n_ij g_i) c_j)  (pivot row: RN(a_i h_ij))
-//   w_j = csum_i(A_ij k_i);  u_j = RN(beta RN(v_j - w_j))
-//   M_ij = fma(k_i, u_j, A_ij);  o_j = csum_i(M_ij q_i)
-//   c'_j = H(max_i |M_ij|);  Z_ij = RN(M_ij RN(1/c'_j))
-//   r'_i = Hup(RN(max_j |Z_ij| / qmax_i)) (smallest fp16 not below; fp32 row
-//   scales: RN);  n'_ij = rne(Z_ij RN(1/r'_i)) -- rounding the step up keeps
-//   |n'| <= qmax, so the clamp is applied only to a row whose step saturated.
-// csum: blocks of 8 rows as fma chains from RN(x0 y0), block sums left to right.
-// Codes are offset binary (u = n + 2^(b-1)) in LSB-first row bit streams.
-#include <hip/hip_fp16.h>
-
-#include "stq_internal.h"
+// HIP kernels for gfx950: per-step decode, pack, unpack and pool init of the
+// quantized recurrent state.  The arithmetic and the thread layout are
+// described in stq_device.h.
+#include "stq_device.h"
 
 namespace stq {
+using namespace dev;
 namespace {
-
-constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic rounds x to an integer (|x| < 2^22)
-
-__device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
-
-// H(x): fp16 nearest-even after saturating to +-65504; returns the pattern.
-__device__ __forceinline__ uint32_t h16(float x) {
-    x = fminf(fmaxf(x, -65504.0f), 65504.0f);
-    return (uint32_t)__half_as_ushort(__float2half_rn(x));
-}
-__device__ __forceinline__ float f16v(uint32_t bits) {
-    return __half2float(__ushort_as_half((unsigned short)(bits & 0xffffu)));
-}
-
-// Hup(x), x >= 0: the smallest fp16 not below x, saturating at 65504.
-__device__ __forceinline__ uint32_t h16up(float x) {
-    uint32_t h = h16(x);
-    if (f16v(h) < x && h != 0x7bffu) ++h;
-    return h;
-}
-
-// Hides a value from the optimizer so byte extractions stay v_cvt_f32_ubyteN.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-    asm("" : "+v"(x));
-    return x;
-}
-
-__device__ __forceinline__ float load1(const void *p, int bf16, size_t e) {
-    if (bf16) return __uint_as_float((uint32_t)(static_cast<const uint16_t *>(p)[e]) << 16);
-    return static_cast<const float *>(p)[e];
-}
-
-// The piece of a row owned by column group cg: 8 codes of w bits = w bytes.
-__device__ __forceinline__ uint4 load_piece(const uint8_t *row, int cg, int w) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    if (w == 4) {
-        r.x = *reinterpret_cast<const uint32_t *>(row + 4 * cg);
-    } else if (w == 8) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(row + 8 * cg);
-        r.x = v.x; r.y = v.y;
-    } else if (w == 6) {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(row + 6 * cg);
-        r.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
-        r.y = p[2];
-    } else {
-        r = *reinterpret_cast<const uint4 *>(row + 16 * cg);
-    }
-    return r;
-}
-
-__device__ __forceinline__ void store_piece(uint8_t *row, int cg, int w, uint4 r) {
-    if (w == 4) {
-        *reinterpret_cast<uint32_t *>(row + 4 * cg) = r.x;
-    } else if (w == 8) {
-        *reinterpret_cast<uint2 *>(row + 8 * cg) = make_uint2(r.x, r.y);
-    } else if (w == 6) {
-        uint16_t *p = reinterpret_cast<uint16_t *>(row + 6 * cg);
-        p[0] = (uint16_t)(r.x & 0xffffu);
-        p[1] = (uint16_t)(r.x >> 16);
-        p[2] = (uint16_t)(r.y & 0xffffu);
-    } else {
-        *reinterpret_cast<uint4 *>(row + 16 * cg) = r;
-    }
-}
-
-// Unsigned (offset-binary) codes of a piece as floats.  For 4-bit pieces the
-// odd codes come out multiplied by 16 (their nibble stays in place); the
-// caller scales them by g/16, which is exact.
-__device__ __forceinline__ void codes_f(uint4 r, int w, float u[8]) {
-    if (w == 4) {
-        const uint32_t lo = opaque(r.x & 0x0F0F0F0Fu), hi = opaque(r.x & 0xF0F0F0F0u);
-        u[0] = (float)(lo & 0xffu);         u[1] = (float)(hi & 0xffu);
-        u[2] = (float)((lo >> 8) & 0xffu);  u[3] = (float)((hi >> 8) & 0xffu);
-        u[4] = (float)((lo >> 16) & 0xffu); u[5] = (float)((hi >> 16) & 0xffu);
-        u[6] = (float)(lo >> 24);           u[7] = (float)(hi >> 24);
-    } else if (w == 8) {
-        const uint32_t x = opaque(r.x), y = opaque(r.y);
-        u[0] = (float)(x & 0xffu);         u[1] = (float)((x >> 8) & 0xffu);
-        u[2] = (float)((x >> 16) & 0xffu); u[3] = (float)(x >> 24);
-        u[4] = (float)(y & 0xffu);         u[5] = (float)((y >> 8) & 0xffu);
-        u[6] = (float)((y >> 16) & 0xffu); u[7] = (float)(y >> 24);
-    } else {  // 6
-        const uint64_t v = (uint64_t)r.x | ((uint64_t)r.y << 32);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) u[c] = (float)(uint32_t)((v >> (6 * c)) & 63u);
-    }
-}
-
-// Codes scaled by the row step: RN((u - 2^(w-1)) * g), with u, g and the
-// offset term exact, so one fma rounds once.  g16 = g / 16, nog = -2^(w-1) g.
-__device__ __forceinline__ void dequant_row(uint4 raw, int w, float g, float g16, float nog, float x[8]) {
-    float u[8];
-    codes_f(raw, w, u);
-    if (w == 4) {
-#pragma unroll
-        for (int c = 0; c < 8; c += 2) {
-            x[c] = fma_(u[c], g, nog);
-            x[c + 1] = fma_(u[c + 1], g16, nog);
-        }
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) x[c] = fma_(u[c], g, nog);
-    }
-}
-
-// Pack 8 quantized values y = 1.5*2^23 + 2^(w-1) + n into a piece: the low
-// byte of each pattern is the offset-binary code (no carry out of the field).
-__device__ __forceinline__ uint4 pack_codes(const float y[8], int w) {
-    uint4 r = make_uint4(0, 0, 0, 0);
-    uint32_t b[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) b[c] = __float_as_uint(y[c]);
-    if (w == 4) {
-        // byte 0 of each pair word = two nibbles, byte 1 = 0
-        const uint32_t p01 = (b[1] << 4) | b[0], p23 = (b[3] << 4) | b[2];
-        const uint32_t p45 = (b[5] << 4) | b[4], p67 = (b[7] << 4) | b[6];
-        r.x = __builtin_amdgcn_perm(p23, p01, 0x0c0c0400u) | __builtin_amdgcn_perm(p67, p45, 0x04000c0cu);
-    } else if (w == 8) {
-        // byte 1 of each pattern is 0, so a shifted or keeps two clean bytes
-        const uint32_t p01 = (b[1] << 8) | b[0], p23 = (b[3] << 8) | b[2];
-        const uint32_t p45 = (b[5] << 8) | b[4], p67 = (b[7] << 8) | b[6];
-        r.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
-        r.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
-    } else {  // 6
-        uint32_t u[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) u[c] = b[c] & 63u;
-        r.x = u[0] | (u[1] << 6) | (u[2] << 12) | (u[3] << 18) | (u[4] << 24) | (u[5] << 30);
-        r.y = (u[5] >> 2) | (u[6] << 4) | (u[7] << 10);
-    }
-    return r;
-}
-
-// LDS of one workgroup.  The per-thread partials are stored element-major,
-// thread-minor ([c][t], with t = rg * d_v/8 + cg): each write of the 64 lanes of
-// a wave is then one contiguous run, and the 4-float pad spreads the combining
-// reads (a column's partials sit at [j % 8][rg * d_v/8 + j / 8]; a row's at
-// [i % 8][i / 8 * d_v/8 + cg]) over the banks.
-template <int DK, int DV>
-struct Lds {
-    static constexpr int NT = DK * DV / 64;
-    static constexpr int NTP = NT + 4;
-    float colp[8][NTP];         // column partial sums: [c][t]
-    union {
-        float colm[8][NTP];     // column partial maxima: [c][t]
-        float rowm[8][NTP];     // row partial maxima: [r][t] (after the column maxima are used)
-    };
-    float g[DK];                // per key row: gated row step RN(a r)
-    float g16[DK];              //   g / 16
-    float nog[DK];              //   -2^(w-1) g
-    float af[DK];               //   gate
-    float kf[DK], qf[DK];       //   k and q as fp32
-    float cf[DV];               // column scales (1 when absent)
-    float u[DV];                // u = beta (v - w)
-    float ic[DV];               // 1 / c'
-    float ir[DK];               // 1 / r'; negated when the row step saturated
-};
-
-// Left-to-right sum of the d_k/8 block partials of column j.
-template <int DK, int DV>
-__device__ __forceinline__ float col_sum(const Lds<DK, DV> &sm, int j) {
-    constexpr int CG = DV / 8, RG = DK / 8;
-    const float *p = &sm.colp[j & 7][j >> 3];
-    float s = p[0];
-#pragma unroll
-    for (int g = 1; g < RG; ++g) s = s + p[g * CG];
-    return s;
-}
-
-template <int DK, int DV>
-__device__ __forceinline__ float col_max(const Lds<DK, DV> &sm, int j) {
-    constexpr int CG = DV / 8, RG = DK / 8;
-    const float *p = &sm.colm[j & 7][j >> 3];
-    float m = p[0];
-#pragma unroll
-    for (int g = 1; g < RG; ++g) m = fmaxf(m, p[g * CG]);
-    return m;
-}
-
-template <int DK, int DV>
-__device__ __forceinline__ float row_max(const Lds<DK, DV> &sm, int i) {
-    constexpr int CG = DV / 8;
-    const float *p = &sm.rowm[i & 7][(i >> 3) * CG];
-    float m = p[0];
-#pragma unroll
-    for (int g = 1; g < CG; ++g) m = fmaxf(m, p[g]);
-    return m;
-}
-
-// Per-thread view of one state during a step / pack.
-struct Rows {
-    int w[8];        // width of each of the thread's rows
-    uint32_t ro[8];  // byte offset of each row inside the head region
-};
-
-template <int DV, int W>
-__device__ __forceinline__ void row_geometry(const Args &A, const HeadDesc &hd, int rg, Rows &rw) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        if (W) {
-            rw.w[r] = W;
-            rw.ro[r] = (uint32_t)(8 * rg + r) * (uint32_t)(DV * W / 8);
-        } else {
-            const uint32_t e = A.rows[hd.rows + 8 * rg + r];
-            rw.w[r] = (int)row_width(e);
-            rw.ro[r] = row_off(e);
-        }
-    }
-}
-
-// Width of key row i of the head (uniform width or the row table).
-template <int W>
-__device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i) {
-    return W ? W : (int)row_width(A.rows[hd.rows + i]);
-}
-
-// Whether the head has quantized rows: known from the width unless rows differ.
-template <int W>
-__device__ __forceinline__ bool has_quant(const HeadDesc &hd) {
-    return W == 16 ? false : (W != 0 ? true : hd.nquant > 0);
-}
-
-template <int N>
-__device__ __forceinline__ void lds_read8(const float *p, float (&out)[N], int o) {
-    const float4 a = reinterpret_cast<const float4 *>(p)[0];
-    const float4 b = reinterpret_cast<const float4 *>(p)[1];
-    out[o + 0] = a.x; out[o + 1] = a.y; out[o + 2] = a.z; out[o + 3] = a.w;
-    out[o + 4] = b.x; out[o + 5] = b.y; out[o + 6] = b.z; out[o + 7] = b.w;
-}
-
-__device__ __forceinline__ uint4 pivot_piece(const float (&x)[8]) {
-    uint4 p;
-    p.x = h16(x[0]) | (h16(x[1]) << 16);
-    p.y = h16(x[2]) | (h16(x[3]) << 16);
-    p.z = h16(x[4]) | (h16(x[5]) << 16);
-    p.w = h16(x[6]) | (h16(x[7]) << 16);
-    return p;
-}
-
-// Quantize one row of 8 values with 1/r' = ir and store the piece.
-template <bool CLAMP>
-__device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir, const float (&x)[8]) {
-    const float off = (float)(1 << (w - 1));
-    const float mg = kMagic + off;
-    float y[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        y[c] = fma_(x[c], ir, mg);
-        if (CLAMP) y[c] = fminf(fmaxf(y[c], mg - (off - 1.0f)), mg + (off - 1.0f));
-    }
-    store_piece(row, cg, w, pack_codes(y, w));
-}
-
-// Column scales, row scales, codes and pivots of x (the thread's 8x8 block of
-// the fp32 state) written back into the head region R.  If emit_o, the column
-// partial sums of o are already in sm.colp and o is combined and stored in the
-// same LDS round as the column maxima.
-template <int DK, int DV, int W>
-__device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd, uint8_t *R,
-                                              const Rows &rw, float (&x)[8][8], Lds<DK, DV> &sm,
-                                              int t, int rg, int cg, bool emit_o, size_t unit) {
-    const bool quant = has_quant<W>(hd);
-    const bool cs = quant && A.cs16;
-    // column maxima over quantized rows
-    if (cs) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float m = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (rw.w[r] != 16) m = fmaxf(m, fabsf(x[r][c]));
-            sm.colm[c][t] = m;
-        }
-    }
-    if (cs || emit_o) __syncthreads();
-    if (t < DV) {
-        if (emit_o) A.o[unit * DV + t] = col_sum<DK, DV>(sm, t);
-        float ic = 1.0f;
-        if (cs) {
-            const float C = col_max<DK, DV>(sm, t);
-            const uint32_t hc = h16(C);
-            const float cv = f16v(hc);
-            ic = cv > 0.0f ? 1.0f / cv : 0.0f;
-            reinterpret_cast<uint16_t *>(R + hd.cs)[t] = (uint16_t)hc;
-        }
-        sm.ic[t] = ic;
-    }
-    if (!quant) {
-        // all rows are FP16 pivots: store and finish
-#pragma unroll
-        for (int r = 0; r < 8; ++r) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
-        return;
-    }
-    __syncthreads();
-    float icc[8];
-    lds_read8(&sm.ic[8 * cg], icc, 0);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        float m = 0.0f;
-        if (rw.w[r] != 16) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float z = x[r][c] * icc[c];
-                x[r][c] = z;
-                m = fmaxf(m, fabsf(z));
-            }
-        }
-        sm.rowm[r][t] = m;
-    }
-    __syncthreads();
-    if (t < DK) {
-        const int w = width_of<W>(A, hd, t);
-        float ir = 0.0f, rv = 0.0f;
-        bool sat = false;
-        if (w != 16) {
-            const float Rm = row_max<DK, DV>(sm, t);
-            const float rq = Rm / (float)((1 << (w - 1)) - 1);
-            if (A.rs16) {
-                rv = f16v(h16up(rq));
-                sat = rq > 65504.0f;
-            } else {
-                rv = rq;
-            }
-            ir = rv > 0.0f ? 1.0f / rv : 0.0f;
-            if (__builtin_isinf(ir)) ir = 0.0f;
-        }
-        if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)h16(rv);
-        else reinterpret_cast<float *>(R + hd.rs)[t] = rv;
-        sm.ir[t] = sat ? -ir : ir;
-    }
-    __syncthreads();
-    float irr[8];
-    lds_read8(&sm.ir[8 * rg], irr, 0);
-    bool anysat = false;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) anysat |= irr[r] < 0.0f;
-    if (__builtin_expect(__any(anysat), 0)) {
-        // a row step saturated at 65504: clamp codes to +-qmax
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
-            else quant_row<true>(R + rw.ro[r], cg, rw.w[r], fabsf(irr[r]), x[r]);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
-            else quant_row<false>(R + rw.ro[r], cg, rw.w[r], irr[r], x[r]);
-        }
-    }
-}
 
 // ----------------------------------------------------------------- step
 

@@ -1,0 +1,706 @@
+// Windowed decode for gfx950 (LeapQuant article, "研究の概要": the low-bit
+// state is requantized only at the end of a window of W tokens; inside the
+// window outputs come from the fixed low-bit base plus updates kept in high
+// precision; large outliers are kept as a few high-precision "compensation"
+// entries that ride the ordinary update path).
+//
+// Per state and step, with n deltas stored (cumulative gate g, deltas
+// (u_m, kap_m) for m < n, base B = RN(n_ij r_i c_j), compensation entries
+// (p = j*d_k + i, val) sorted by p):
+//   kap_m <- RN(kap_m a), g <- RN(g a), kg = RN(g k), qg = RN(g q)
+//   w_j = csum(B_.j, kg); for each entry of column j: w_j = fma(val, kg_i, w_j);
+//         w_j = fma(u_m,j, csum(kap_m, k), w_j) for m < n
+//   u = RN(beta RN(v - w)); store (u, k) as delta n
+//   o_j: the same with q, over m <= n
+//   if n + 1 == W: D = RN(kap_0 u_0^T) then fma over m; M = fma(g, B + entries, D);
+//         the K largest |M| (ties: lower p) become the new entries, the rest
+//         is requantized as in the per-step mode; g = 1, n = 0.
+//
+// Thread layout as in the per-step kernel (8 x 8 block per thread, one
+// workgroup per state).  Delta keys are decayed and dotted with k and q by
+// (delta, 8-row block) pairs.  At the window end the deltas are staged in LDS
+// (window <= 16) and D is accumulated in the registers that held the base.
+#include "stq_device.h"
+
+namespace stq {
+using namespace dev;
+namespace {
+
+constexpr int kWMax = 16;     // window length supported by the LDS staging
+constexpr int kKMax = 1024;   // compensation entries
+constexpr int kCandMax = 1024;  // top-K candidates ranked exactly
+
+template <int DK, int DV>
+struct LdsW {
+    Lds<DK, DV> b;            // per-step arrays (partials, row/column constants, 1/c', 1/r')
+    float kr[DK], qr[DK];     // k and q as fp32
+    float gn[DK];             // cumulative gate after this step
+    float ckp[kWMax][DK / 8], cqp[kWMax][DK / 8];  // csum block partials of kap_m . k, kap_m . q
+    float ck[kWMax], cq[kWMax];
+    float kst[kWMax][DK];     // decayed delta keys (window end)
+    float ust[kWMax][DV];     // delta values
+    uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
+    float cvl[kKMax];         // compensation value
+    uint32_t ckey[kCandMax];  // candidate keys
+    int red[2][8];            // block reductions
+    uint32_t bc[4];           // broadcasts
+};
+
+// Block-wide sum of one int per thread (alternating buffers: one barrier).
+template <int NT>
+__device__ __forceinline__ int block_sum(int v, int (&red)[2][8], int &phase) {
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int t = threadIdx.x;
+    if ((t & 63) == 0) red[phase][t >> 6] = v;
+    __syncthreads();
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[phase][w];
+    phase ^= 1;
+    return s;
+}
+
+// First index e in [0, n) with a[e] >= x (a sorted ascending).
+__device__ __forceinline__ int lower_bound(const uint32_t *a, int n, uint32_t x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Selection works on magnitudes |M| of entries of quantized rows; for finite
+// non-negative floats the bit patterns order like the values, which the
+// fallback search uses.  Linear index p = j*d_k + i; the thread's entry (r, c)
+// has p = pbase + c*d_k + r with pbase = 8*cg*d_k + 8*rg.
+
+// Number of the thread's quantized entries with |M| >= thr.
+__device__ __forceinline__ int count_ge(const float (&x)[8][8], const Rows &rw, float thr) {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) n += (rw.w[r] != 16) & (fabsf(x[r][c]) >= thr);
+    return n;
+}
+
+// Is (|M|, p) of the thread's entry (r, c) among the first K in the order
+// (|M| descending, p ascending), given the K-th entry (thr, pk)?
+template <int DK>
+__device__ __forceinline__ bool chosen(float v, uint32_t p, float thr, uint32_t pk) {
+    return (v > thr) || (v == thr && p <= pk);
+}
+
+// Select the K entries of largest |M| (ties: lower p) among the quantized rows
+// of the state held in x; write them sorted by p to the head's compensation
+// arrays and set them to 0 in x (so they are left out of both scale maxima
+// and get code 0).
+template <int DK, int DV>
+__device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, const Rows &rw,
+                             float (&x)[8][8], LdsW<DK, DV> &sm, int t, int rg, int cg) {
+    constexpr int NT = DK * DV / 64;
+    const int K = A.comps;
+    if (K <= 0) return;
+    const uint32_t pbase = (uint32_t)(8 * cg * DK + 8 * rg);
+    int phase = 0;
+    float thr = 0.0f;        // the K-th entry is (thr, pk)
+    uint32_t pk = 0;
+    bool exact = false;
+
+    // 1) the K-th largest of the per-thread maxima bounds the K-th |M| from below
+    float tmax = -1.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (rw.w[r] != 16) tmax = fmaxf(tmax, fabsf(x[r][c]));
+    if (K <= NT) {
+        reinterpret_cast<float *>(sm.ckey)[t] = tmax;
+        __syncthreads();
+        int rank = 0;  // thread maxima (value desc, thread asc) ahead of mine
+        for (int s2 = 0; s2 < NT; ++s2) {
+            const float o = reinterpret_cast<const float *>(sm.ckey)[s2];
+            rank += (o > tmax) || (o == tmax && s2 < t);
+        }
+        if (rank == K - 1) sm.bc[0] = __float_as_uint(tmax);
+        __syncthreads();
+        const float t0 = __uint_as_float(sm.bc[0]);
+        // 2) compact the candidates |M| >= t0 into LDS when they are few
+        const int mine = t0 >= 0.0f ? count_ge(x, rw, t0) : 0;
+        const int total = block_sum<NT>(mine, sm.red, phase);
+        if (t0 >= 0.0f && total <= kCandMax) {
+            if (t == 0) sm.bc[1] = 0;
+            __syncthreads();
+            int base = mine ? (int)atomicAdd(&sm.bc[1], (uint32_t)mine) : 0;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float v = fabsf(x[r][c]);
+                    if (rw.w[r] != 16 && v >= t0) {
+                        reinterpret_cast<float *>(sm.ckey)[base] = v;
+                        sm.cix[base] = pbase + (uint32_t)(c * DK + r);
+                        ++base;
+                    }
+                }
+            __syncthreads();
+            // 3) exact rank of every candidate; the K-th one is (thr, pk)
+            for (int e = t; e < total; e += NT) {
+                const float v = reinterpret_cast<const float *>(sm.ckey)[e];
+                const uint32_t p = sm.cix[e];
+                int rank2 = 0;
+                for (int f = 0; f < total; ++f) {
+                    const float v2 = reinterpret_cast<const float *>(sm.ckey)[f];
+                    rank2 += (v2 > v) || (v2 == v && sm.cix[f] < p);
+                }
+                if (rank2 == K - 1) { sm.bc[2] = __float_as_uint(v); sm.bc[3] = p; }
+            }
+            __syncthreads();
+            thr = __uint_as_float(sm.bc[2]);
+            pk = sm.bc[3];
+            exact = true;
+        }
+    }
+    if (!exact) {
+        // fallback: bit-serial search of the K-th |M| over the whole state,
+        // then of the tie position
+        uint32_t P = 0;
+        for (int bit = 30; bit >= 0; --bit) {
+            const uint32_t cand = P | (1u << bit);
+            if (block_sum<NT>(count_ge(x, rw, __uint_as_float(cand)), sm.red, phase) >= K) P = cand;
+        }
+        thr = __uint_as_float(P);
+        int above = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) above += (rw.w[r] != 16) & (fabsf(x[r][c]) > thr);
+        const int need = K - block_sum<NT>(above, sm.red, phase);
+        uint32_t X = 0;
+        for (int bit = 15; bit >= 0; --bit) {
+            const uint32_t cand = X | (1u << bit);
+            int m2 = 0;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    m2 += (rw.w[r] != 16) & (fabsf(x[r][c]) == thr) & (pbase + (uint32_t)(c * DK + r) < cand);
+            if (block_sum<NT>(m2, sm.red, phase) < need) X = cand;
+        }
+        pk = X;
+    }
+
+    // the chosen entries, then ranked by p for storage
+    if (t == 0) sm.bc[1] = 0;
+    __syncthreads();
+    int mine = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            mine += (rw.w[r] != 16) & chosen<DK>(fabsf(x[r][c]), pbase + (uint32_t)(c * DK + r), thr, pk);
+    int base = mine ? (int)atomicAdd(&sm.bc[1], (uint32_t)mine) : 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const uint32_t p = pbase + (uint32_t)(c * DK + r);
+            if (rw.w[r] != 16 && chosen<DK>(fabsf(x[r][c]), p, thr, pk)) {
+                sm.cix[base] = p;
+                sm.cvl[base] = x[r][c];
+                ++base;
+                x[r][c] = 0.0f;
+            }
+        }
+    __syncthreads();
+    for (int e = t; e < K; e += NT) {
+        const uint32_t p = sm.cix[e];
+        int rank = 0;
+        for (int f = 0; f < K; ++f) rank += sm.cix[f] < p;
+        reinterpret_cast<uint16_t *>(R + hd.cidx)[rank] = (uint16_t)p;
+        reinterpret_cast<float *>(R + hd.cval)[rank] = sm.cvl[e];
+    }
+    __syncthreads();
+}
+
+// Base B of one row piece: RN(RN(n r) c) for a quantized row (n r is exact),
+// the stored fp16 values for a pivot row.  No compensation entries.
+template <int DK, int DV>
+__device__ __forceinline__ void base_row(int w, uint4 raw, const LdsW<DK, DV> &sm, int i,
+                                         const float (&cc)[8], float (&x)[8]) {
+    if (w == 16) {
+        const uint32_t hv[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            x[2 * c] = f16v(hv[c]);
+            x[2 * c + 1] = f16v(hv[c] >> 16);
+        }
+    } else {
+        dequant_row(raw, w, sm.b.g[i], sm.b.g16[i], sm.b.nog[i], x);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = x[c] * cc[c];
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void base_block(const Rows &rw, const uint4 (&raw)[8], const LdsW<DK, DV> &sm,
+                                           int rg, const float (&cc)[8], float (&x)[8][8]) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) base_row<DK, DV>(rw.w[r], raw[r], sm, 8 * rg + r, cc, x[r]);
+}
+
+// Row and column constants of the base dequantization (row scale r: in g,
+// r/16 in g16, -2^(w-1) r in nog; column scales in cf).
+template <int DK, int DV, int W>
+__device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd, const uint8_t *R,
+                                               LdsW<DK, DV> &sm, int t) {
+    const bool quant = has_quant<W>(hd);
+    if (t < DK) {
+        const int w = width_of<W>(A, hd, t);
+        float ri = 0.0f;
+        if (quant && w != 16)
+            ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[t])
+                        : reinterpret_cast<const float *>(R + hd.rs)[t];
+        sm.b.g[t] = ri;
+        sm.b.g16[t] = ri * 0.0625f;
+        sm.b.nog[t] = w != 16 ? -(float)(1 << (w - 1)) * ri : 0.0f;
+    }
+    if (t < DV)
+        sm.b.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+}
+
+template <int DK, int DV, int W>
+__device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
+                                         LdsW<DK, DV> &sm, int t, int rg, int cg) {
+    constexpr int NT = DK * DV / 64, RG = DK / 8;
+    const int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
+    const int W_ = A.window;
+    if (n < 0 || n >= W_) {
+        // a delta count outside [0, W) is not a state this library wrote
+        if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
+        return;
+    }
+    const int K = A.comps;
+    Rows rw;
+    row_geometry<DV, W>(A, hd, rg, rw);
+    uint4 raw[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+    float *gmem = reinterpret_cast<float *>(R + hd.g);
+    float *du = reinterpret_cast<float *>(R + hd.du);
+    float *dkap = reinterpret_cast<float *>(R + hd.dkap);
+
+    // per key row / value column constants and the stored delta values
+    base_constants<DK, DV, W>(A, hd, R, sm, t);
+    const float beta = A.beta[unit];
+    float vv = 0.0f;
+    if (t < DK) {
+        const float a = A.gate_vec ? A.a[unit * DK + t] : A.a[unit];
+        const float k = load1(A.k, A.io_bf16, unit * DK + t);
+        const float q = load1(A.q, A.io_bf16, unit * DK + t);
+        const float g = gmem[t] * a;
+        sm.b.af[t] = a;
+        sm.kr[t] = k;
+        sm.qr[t] = q;
+        sm.gn[t] = g;
+        sm.b.kf[t] = g * k;
+        sm.b.qf[t] = g * q;
+        gmem[t] = g;
+    }
+    if (t < DV) {
+        vv = load1(A.v, A.io_bf16, unit * DV + t);
+        for (int m = 0; m < n; ++m) sm.ust[m][t] = du[(size_t)m * DV + t];
+    }
+    for (int e = t; e < K; e += NT) {
+        sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
+        sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+    }
+    __syncthreads();
+
+    // delta keys: decay, store back, block partials of kap . k and kap . q
+    for (int pr = t; pr < (n + 1) * RG; pr += NT) {
+        const int m = pr / RG, blk = pr - m * RG, i0 = 8 * blk;
+        float kap[8];
+        if (m < n) {
+            float4 *p = reinterpret_cast<float4 *>(dkap + (size_t)m * DK + i0);
+            const float4 a0 = p[0], a1 = p[1];
+            kap[0] = a0.x; kap[1] = a0.y; kap[2] = a0.z; kap[3] = a0.w;
+            kap[4] = a1.x; kap[5] = a1.y; kap[6] = a1.z; kap[7] = a1.w;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) kap[r] = kap[r] * sm.b.af[i0 + r];
+            p[0] = make_float4(kap[0], kap[1], kap[2], kap[3]);
+            p[1] = make_float4(kap[4], kap[5], kap[6], kap[7]);
+            float s = kap[0] * sm.kr[i0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r) s = fma_(kap[r], sm.kr[i0 + r], s);
+            sm.ckp[m][blk] = s;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) kap[r] = sm.kr[i0 + r];
+        }
+        float s = kap[0] * sm.qr[i0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) s = fma_(kap[r], sm.qr[i0 + r], s);
+        sm.cqp[m][blk] = s;
+    }
+
+    // base read / output partials
+    float cc[8], kk[8], qq[8];
+    lds_read8(&sm.b.cf[8 * cg], cc, 0);
+    lds_read8(&sm.b.kf[8 * rg], kk, 0);
+    lds_read8(&sm.b.qf[8 * rg], qq, 0);
+    float x[8][8];
+    base_block<DK, DV>(rw, raw, sm, rg, cc, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float s = x[0][c] * kk[0], s2 = x[0][c] * qq[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) {
+            s = fma_(x[r][c], kk[r], s);
+            s2 = fma_(x[r][c], qq[r], s2);
+        }
+        sm.b.colp[c][t] = s;
+        sm.b.colm[c][t] = s2;
+    }
+    __syncthreads();
+    float w0 = 0.0f, o0 = 0.0f;
+    if (t < DV) {
+        w0 = col_sum<DK, DV>(sm.b, t);
+        const float *p = &sm.b.colm[t & 7][t >> 3];
+        o0 = p[0];
+#pragma unroll
+        for (int g = 1; g < RG; ++g) o0 = o0 + p[g * (DV / 8)];
+    }
+    if (t <= n) {
+        float s = 0.0f, s2 = sm.cqp[t][0];
+        if (t < n) s = sm.ckp[t][0];
+#pragma unroll
+        for (int g = 1; g < RG; ++g) {
+            if (t < n) s = s + sm.ckp[t][g];
+            s2 = s2 + sm.cqp[t][g];
+        }
+        sm.ck[t] = s;
+        sm.cq[t] = s2;
+    }
+    __syncthreads();
+
+    if (t < DV) {
+        const int j = t;
+        const int lo = lower_bound(sm.cix, K, (uint32_t)(j * DK));
+        const int hi = lower_bound(sm.cix, K, (uint32_t)((j + 1) * DK));
+        float w = w0;
+        for (int e = lo; e < hi; ++e) w = fma_(sm.cvl[e], sm.b.kf[sm.cix[e] - j * DK], w);
+        for (int m = 0; m < n; ++m) w = fma_(sm.ust[m][j], sm.ck[m], w);
+        const float u = beta * (vv - w);
+        du[(size_t)n * DV + j] = u;
+        float o = o0;
+        for (int e = lo; e < hi; ++e) o = fma_(sm.cvl[e], sm.b.qf[sm.cix[e] - j * DK], o);
+        for (int m = 0; m < n; ++m) o = fma_(sm.ust[m][j], sm.cq[m], o);
+        o = fma_(u, sm.cq[n], o);
+        A.o[unit * DV + j] = o;
+    }
+    if (t < DK) dkap[(size_t)n * DK + t] = sm.kr[t];
+    // at the W-th delta the count reaches W; the window-end kernel closes it
+    if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = n + 1;
+}
+
+// Window end of one state holding W deltas: M = fma(g, B + entries, D) with
+// D = RN(kap_0 u_0^T) then fma over the deltas; the K largest |M| become the
+// new compensation entries, the rest is requantized; g = 1, n = 0.
+template <int DK, int DV, int W>
+__device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
+                                         LdsW<DK, DV> &sm, int t, int rg, int cg) {
+    constexpr int NT = DK * DV / 64;
+    const int n = A.window;
+    const int K = A.comps;
+    Rows rw;
+    row_geometry<DV, W>(A, hd, rg, rw);
+    uint4 raw[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+    float *gmem = reinterpret_cast<float *>(R + hd.g);
+    const float *du = reinterpret_cast<const float *>(R + hd.du);
+    const float *dkap = reinterpret_cast<const float *>(R + hd.dkap);
+    base_constants<DK, DV, W>(A, hd, R, sm, t);
+    for (int e = t; e < n * DK; e += NT) sm.kst[e / DK][e % DK] = dkap[e];
+    for (int e = t; e < n * DV; e += NT) sm.ust[e / DV][e % DV] = du[e];
+    if (t < DK) sm.gn[t] = gmem[t];
+    for (int e = t; e < K; e += NT) {
+        sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
+        sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+    }
+    __syncthreads();
+    float x[8][8];
+    {
+        float kq[8], uq[8];
+        lds_read8(&sm.kst[0][8 * rg], kq, 0);
+        lds_read8(&sm.ust[0][8 * cg], uq, 0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[r][c] = kq[r] * uq[c];
+        for (int m = 1; m < n; ++m) {
+            lds_read8(&sm.kst[m][8 * rg], kq, 0);
+            lds_read8(&sm.ust[m][8 * cg], uq, 0);
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[r][c] = fma_(kq[r], uq[c], x[r][c]);
+        }
+    }
+    float gg[8], cc[8];
+    lds_read8(&sm.gn[8 * rg], gg, 0);
+    lds_read8(&sm.b.cf[8 * cg], cc, 0);
+    // M = fma(g, B, D): compensation entries at their positions first
+    uint64_t done = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t p0 = (uint32_t)((8 * cg + c) * DK + 8 * rg);
+        const int lo = lower_bound(sm.cix, K, p0);
+        for (int e = lo; e < K && sm.cix[e] < p0 + 8; ++e) {
+            const int rr = (int)(sm.cix[e] - p0);
+            const float val = sm.cvl[e];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r == rr) x[r][c] = fma_(gg[r], val, x[r][c]);
+            done |= 1ull << (rr * 8 + c);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float B[8];
+        base_row<DK, DV>(rw.w[r], raw[r], sm, 8 * rg + r, cc, B);
+        const uint32_t dr = (uint32_t)(done >> (8 * r)) & 0xffu;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            if (!((dr >> c) & 1u)) x[r][c] = fma_(gg[r], B[c], x[r][c]);
+    }
+    __syncthreads();  // old entries are no longer read from LDS
+    select_comps<DK, DV>(A, hd, R, rw, x, sm, t, rg, cg);
+    requant_store<DK, DV, W>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
+    if (t < DK) gmem[t] = 1.0f;
+    if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = 0;
+}
+
+template <int DK, int DV, bool MIXED>
+__global__ void __launch_bounds__(DK * DV / 64) k_win_end(Args A) {
+    constexpr int CG = DV / 8;
+    __shared__ LdsW<DK, DV> sm;
+    const size_t unit = blockIdx.x;
+    const int b = (int)(unit / (size_t)A.H);
+    const int h = (int)(unit - (size_t)b * A.H);
+    const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
+    const int slot = A.slot_ids[b];
+    if (slot < 0 || slot >= A.nslots) return;
+    const HeadDesc &hd = A.heads[h];
+    uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
+    if (*reinterpret_cast<const int32_t *>(R + hd.wn) != A.window) return;
+    switch (hd.width) {
+        case 4: end_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 6: end_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 8: end_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 16: end_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+        default:
+            if (MIXED) end_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            break;
+    }
+}
+
+template <int DK, int DV, bool MIXED>
+__global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
+    constexpr int CG = DV / 8;
+    __shared__ LdsW<DK, DV> sm;
+    const size_t unit = blockIdx.x;
+    const int b = (int)(unit / (size_t)A.H);
+    const int h = (int)(unit - (size_t)b * A.H);
+    const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
+    const int slot = A.slot_ids[b];
+    if (slot < 0 || slot >= A.nslots) {
+        if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
+        return;
+    }
+    const HeadDesc &hd = A.heads[h];
+    uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
+    switch (hd.width) {
+        case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 16: win_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+        default:
+            if (MIXED) win_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            break;
+    }
+}
+
+// stq_pack for the windowed layout: compensation entries chosen from the fp32
+// state, the rest requantized, g = 1, no deltas (delta storage cleared).
+template <int DK, int DV, int W>
+__device__ __forceinline__ void pack_win_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
+                                              LdsW<DK, DV> &sm, int t, int rg, int cg) {
+    constexpr int NT = DK * DV / 64;
+    Rows rw;
+    row_geometry<DV, W>(A, hd, rg, rw);
+    float x[8][8];
+    const float *src = A.state + unit * DK * DV;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float4 *p = reinterpret_cast<const float4 *>(src + (size_t)(8 * rg + r) * DV + 8 * cg);
+        const float4 a = p[0], b = p[1];
+        x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
+        x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
+    }
+    select_comps<DK, DV>(A, hd, R, rw, x, sm, t, rg, cg);
+    requant_store<DK, DV, W>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
+    float *g = reinterpret_cast<float *>(R + hd.g);
+    float *du = reinterpret_cast<float *>(R + hd.du);
+    float *dkap = reinterpret_cast<float *>(R + hd.dkap);
+    for (int i = t; i < DK; i += NT) g[i] = 1.0f;
+    for (int e = t; e < A.window * DV; e += NT) du[e] = 0.0f;
+    for (int e = t; e < A.window * DK; e += NT) dkap[e] = 0.0f;
+    if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = 0;
+}
+
+template <int DK, int DV, bool MIXED>
+__global__ void __launch_bounds__(DK * DV / 64) k_pack_win(Args A) {
+    constexpr int CG = DV / 8;
+    __shared__ LdsW<DK, DV> sm;
+    const size_t unit = blockIdx.x;
+    const int b = (int)(unit / (size_t)A.H);
+    const int h = (int)(unit - (size_t)b * A.H);
+    const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
+    const int slot = A.slot_ids[b];
+    if (slot < 0 || slot >= A.nslots) return;
+    const HeadDesc &hd = A.heads[h];
+    uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
+    switch (hd.width) {
+        case 4: pack_win_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 6: pack_win_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 8: pack_win_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 16: pack_win_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+        default:
+            if (MIXED) pack_win_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            break;
+    }
+}
+
+// stq_unpack for the windowed layout: M = fma(g, B + entries, D) with D the
+// stored deltas (or B alone when there are none).
+template <int DK, int DV>
+__global__ void __launch_bounds__(DK * DV / 64) k_unpack_win(Args A) {
+    constexpr int CG = DV / 8;
+    __shared__ LdsW<DK, DV> sm;
+    const size_t unit = blockIdx.x;
+    const int b = (int)(unit / (size_t)A.H);
+    const int h = (int)(unit - (size_t)b * A.H);
+    const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
+    const int slot = A.slot_ids[b];
+    float *dst = A.state + unit * DK * DV;
+    if (slot < 0 || slot >= A.nslots) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) dst[(size_t)(8 * rg + r) * DV + 8 * cg + c] = __builtin_nanf("");
+        return;
+    }
+    const HeadDesc &hd = A.heads[h];
+    const uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
+    int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
+    if (n < 0 || n >= A.window) n = 0;
+    const int K = A.comps;
+    Rows rw;
+    row_geometry<DV, 0>(A, hd, rg, rw);
+    uint4 raw[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+    base_constants<DK, DV, 0>(A, hd, R, sm, t);
+    for (int e = t; e < K; e += DK * DV / 64) {
+        sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
+        sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+    }
+    __syncthreads();
+    float cc[8];
+    lds_read8(&sm.b.cf[8 * cg], cc, 0);
+    float x[8][8];
+    base_block<DK, DV>(rw, raw, sm, rg, cc, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t p0 = (uint32_t)((8 * cg + c) * DK + 8 * rg);
+        const int lo = lower_bound(sm.cix, K, p0);
+        for (int e = lo; e < K && sm.cix[e] < p0 + 8; ++e) {
+            const int rr = (int)(sm.cix[e] - p0);
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r == rr) x[r][c] = sm.cvl[e];
+        }
+    }
+    if (n > 0) {
+        const float *g = reinterpret_cast<const float *>(R + hd.g);
+        const float *du = reinterpret_cast<const float *>(R + hd.du);
+        const float *dkap = reinterpret_cast<const float *>(R + hd.dkap);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int i = 8 * rg + r;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int j = 8 * cg + c;
+                float D = dkap[i] * du[j];
+                for (int m = 1; m < n; ++m) D = fma_(dkap[(size_t)m * DK + i], du[(size_t)m * DV + j], D);
+                x[r][c] = fma_(g[i], x[r][c], D);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float4 *p = reinterpret_cast<float4 *>(dst + (size_t)(8 * rg + r) * DV + 8 * cg);
+        p[0] = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+        p[1] = make_float4(x[r][4], x[r][5], x[r][6], x[r][7]);
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_grid(void (*k)(Args), const Args &a, hipStream_t s) {
+    if (a.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * a.H)), dim3(DK * DV / 64), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#define STQ_WIN_DISPATCH(KERNEL)                                                               \
+    if (dk == 128 && dv == 128)                                                               \
+        return mixed ? launch_grid<128, 128>(KERNEL<128, 128, true>, a, s)                     \
+                     : launch_grid<128, 128>(KERNEL<128, 128, false>, a, s);                   \
+    if (dk == 64 && dv == 64)                                                                 \
+        return mixed ? launch_grid<64, 64>(KERNEL<64, 64, true>, a, s)                         \
+                     : launch_grid<64, 64>(KERNEL<64, 64, false>, a, s);                       \
+    if (dk == 128 && dv == 64)                                                                \
+        return mixed ? launch_grid<128, 64>(KERNEL<128, 64, true>, a, s)                       \
+                     : launch_grid<128, 64>(KERNEL<128, 64, false>, a, s);                     \
+    if (dk == 64 && dv == 128)                                                                \
+        return mixed ? launch_grid<64, 128>(KERNEL<64, 128, true>, a, s)                       \
+                     : launch_grid<64, 128>(KERNEL<64, 128, false>, a, s);                     \
+    return hipErrorInvalidValue;
+
+hipError_t launch_step_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
+    const hipError_t e = [&]() -> hipError_t { STQ_WIN_DISPATCH(k_win) }();
+    if (e != hipSuccess) return e;
+    STQ_WIN_DISPATCH(k_win_end)
+}
+
+hipError_t launch_pack_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
+    STQ_WIN_DISPATCH(k_pack_win)
+}
+
+hipError_t launch_unpack_win(const Args &a, int dk, int dv, hipStream_t s) {
+    if (dk == 128 && dv == 128) return launch_grid<128, 128>(k_unpack_win<128, 128>, a, s);
+    if (dk == 64 && dv == 64) return launch_grid<64, 64>(k_unpack_win<64, 64>, a, s);
+    if (dk == 128 && dv == 64) return launch_grid<128, 64>(k_unpack_win<128, 64>, a, s);
+    if (dk == 64 && dv == 128) return launch_grid<64, 128>(k_unpack_win<64, 128>, a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace stq

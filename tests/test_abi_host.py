@@ -65,7 +65,7 @@ def test_pool_size_query_without_device(stq):
 @pytest.mark.parametrize("field,value,status", [
     ("H", 0, 1), ("d_k", 96, 2), ("d_v", 32, 2), ("unit", 5, 1), ("gate", 2, 1),
     ("row_scale", 0, 1), ("col_scale", 1, 1), ("io_dtype", 2, 1), ("window", 0, 1),
-    ("window", 65, 2), ("comps", 3, 1), ("comps", -1, 1),
+    ("window", 17, 2), ("comps", 3, 1), ("comps", -1, 1),
 ])
 def test_config_rejected(stq, field, value, status):
     bits = np.full(4, 4, np.uint8)

@@ -202,3 +202,78 @@ def test_empty_batch_is_a_noop():
         assert np.array_equal(before, hs.slot_bytes_gpu())
     finally:
         hs.close()
+
+
+# ------------------------------------------------------------ windowed mode
+
+def test_windowed_kda_all_units_two_and_a_half_windows():
+    """8-bit KDA state requantized every 16 tokens with 82 fp32 compensation
+    entries per state: every unit of B=4 x H=32 over 40 steps (two window ends),
+    slot bytes compared after each window end."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=4)
+    _run(w, 40, check_slots_every=8, tag="win-kda")
+
+
+def test_windowed_mixed_rows_d64():
+    """Windowed mode with key rows of every width (and pivot rows), d=64, W=4."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=3, H=4, dk=64, dv=64, window=4, comps=10,
+                                              name="win_mixed_d64")
+    rng = np.random.default_rng(5)
+    bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), w.H * w.dk, p=[0.4, 0.25, 0.25, 0.1])
+    _run(w, 13, bits=bits, check_slots_every=1, tag="win-mixed")
+
+
+def test_windowed_zero_state_ties():
+    """From the empty state every |M| ties at 0 in the first window's selection
+    (and in pack): the lowest indices must win, exactly as in the oracle."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=2, H=4, window=2, comps=40, init="zero",
+                                              name="win_zero")
+    hs = _harness(w)
+    try:
+        import torch
+        import linear_attention_recurrent_stq_amd as stq
+        zero = np.zeros((w.B, w.H, w.dk, w.dv), np.float32)
+        stq.pack(hs.pool, hs.slot_ids, torch.from_numpy(zero).cuda())
+        for b, h in hs.follow:
+            hs.ocfg.pack_head(hs.oslots[b], h, zero[b, h])
+        assert not hs.compare_slots()
+        for t in range(5):
+            o_gpu, o_ref = hs.step(hs.load_full(t))
+            _check_step(o_gpu, o_ref, hs.follow, t, "win-zero")
+            assert not hs.compare_slots(), t
+    finally:
+        hs.close()
+
+
+def test_windowed_unpack_mid_window():
+    """stq_unpack of a windowed state with pending deltas materializes
+    fma(g, B, D) exactly as the oracle."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=2, H=8)
+    hs = _harness(w)
+    try:
+        hs.init_state()
+        for t in range(7):
+            hs.step(hs.load_full(t))
+        got = hs.unpack_gpu()
+        for b, h in hs.follow:
+            assert np.array_equal(got[b, h], hs.ocfg.unpack_head(hs.oslots[b], h)), (b, h)
+    finally:
+        hs.close()
+
+
+def test_windowed_full_batch_sampled_units():
+    """B=512 x H=32 windowed KDA pool, 40 followed units over 3 windows."""
+    w = synth.WORKLOADS["windowed_kda"]
+    rng = np.random.default_rng(6)
+    follow = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 40), rng.integers(0, w.H, 40))})
+    hs = _harness(w, follow=follow)
+    try:
+        hs.init_state()
+        hs.load_full(0)
+        for t in range(48):
+            x = hs.load_followed(t)
+            o_gpu, o_ref = hs.step(x, idx_in_x=True)
+            _check_step(o_gpu, o_ref, hs.follow, t, "win-full")
+        assert not hs.compare_slots()
+    finally:
+        hs.close()
