@@ -54,9 +54,54 @@ def io_bytes(w: synth.Workload) -> int:
     return e * (2 * w.dk + w.dv) + gate + 4 + 4 * w.dv
 
 
-def launch_bytes(w: synth.Workload, bits: np.ndarray) -> int:
-    """Algorithmic HBM bytes of one launch (B requests, all heads of a layer)."""
-    return w.B * (2 * sum(state_bytes(w, bits)) + w.H * io_bytes(w) + 4)
+def launch_bytes(w: synth.Workload, bits: np.ndarray) -> float:
+    """Algorithmic HBM bytes of one launch (B requests, all heads of a layer).
+
+    Every-step mode: each head's stored state is read and written once, plus
+    the per-head inputs and output.  Windowed mode (W tokens, K entries): the
+    average over one window of what a step must touch once -- base state,
+    gate, entries and the n stored deltas read; gate, new delta, decayed keys
+    written; at the window end the new base and entries written.
+    """
+    state = sum(state_bytes(w, bits))
+    io = w.H * io_bytes(w) + 4
+    if w.window == 1:
+        return w.B * (2 * state + io)
+    W, K, dk, dv = w.window, w.comps, w.dk, w.dv
+    per_head = 0.0
+    for n in range(W):
+        rd = 4 * dk + 6 * K + 4 + n * 4 * (dk + dv)
+        wr = 4 * dk + 4 * (dk + dv) + n * 4 * dk + 4
+        per_head += rd + wr
+    per_head += 6 * K  # new entries at the window end
+    return w.B * (state + state / W + w.H * per_head / W + io)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_recurrent_stq_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"k_step_{workload}_counters.txt")
+    try:
+        kv = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
@@ -108,6 +153,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=256)
     ap.add_argument("--cpu-steps", type=int, default=64)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the decode step needs no collective and this "
@@ -158,6 +205,13 @@ def main() -> int:
     for t in range(args.warmup):
         one_step(t)
     torch.cuda.synchronize()
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     K = args.steps
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -209,8 +263,10 @@ def main() -> int:
                       "p50": round(float(np.percentile(launch_ms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_step<128,128>", "bytes_per_launch": int(per_launch_bytes)},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic(w.name),
+                     "kernel": "k_win + k_win_end" if w.window > 1 else "k_step",
+                     "bytes_per_launch": int(per_launch_bytes)},
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
