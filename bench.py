@@ -151,8 +151,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="serving_gdn", choices=list(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=256)
-    ap.add_argument("--cpu-steps", type=int, default=64)
+    ap.add_argument("--cpu-units", type=int, default=512)
+    ap.add_argument("--cpu-steps", type=int, default=96)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="also run a plain device copy of this many bytes (counter calibration)")
     args = ap.parse_args()

@@ -48,6 +48,11 @@ class Harness:
         self.follow = list(follow)
         self.fb = np.array([u[0] for u in self.follow], np.int64)
         self.fh = np.array([u[1] for u in self.follow], np.int64)
+        self.fb_dev = torch.from_numpy(self.fb).cuda()
+        self.fh_dev = torch.from_numpy(self.fh).cuda()
+        self.everything = len(self.follow) == w.B * w.H
+        self.shadow = None  # unquantized fp32 states of the followed units
+        self.shadow_err = []
         reqs = sorted(set(self.fb.tolist()))
         self.oslots = {b: self.ocfg.new_slot() for b in reqs}
         self.exec = ThreadPoolExecutor(THREADS)
@@ -81,8 +86,7 @@ class Harness:
         """Overwrite only the followed units' inputs (others keep what they had)."""
         x = synth.step_inputs(self.w, self.layer, t, self.fb, self.fh)
         q, k, v = self._to_dev(x)
-        bi = self.torch.from_numpy(self.fb).cuda()
-        hi = self.torch.from_numpy(self.fh).cuda()
+        bi, hi = self.fb_dev, self.fh_dev
         self.q[bi, hi] = q.cuda(); self.k[bi, hi] = k.cuda(); self.v[bi, hi] = v.cuda()
         self.a[bi, hi] = self.torch.from_numpy(x.a).cuda()
         self.beta[bi, hi] = self.torch.from_numpy(x.beta).cuda()
@@ -100,11 +104,20 @@ class Harness:
         self.stq.pack(self.pool, self.slot_ids, torch.from_numpy(M0).cuda())
         for b, h in self.follow:
             self.ocfg.pack_head(self.oslots[b], h, M0[b, h])
+        if self.shadow is not None:
+            self.shadow = [np.ascontiguousarray(M0[b, h]) for b, h in self.follow]
+
+    def track_fp32(self):
+        """Also run the unquantized fp32 recurrence for every followed unit
+        (from the same initial state) and record, per step, the largest
+        relative distance of the quantized output from it."""
+        self.shadow = [np.zeros((self.w.dk, self.w.dv), np.float32) for _ in self.follow]
 
     # --------------------------------------------------------------- step
     def step(self, x_followed: synth.StepInputs, idx_in_x=None):
         """One GPU step on the whole batch, one oracle step per followed unit.
-        Returns the GPU o [B,H,dv] and the oracle o per followed unit."""
+        Returns the GPU o of the followed units [n, dv] (gathered on the
+        device) and the oracle o per followed unit."""
         self.stq.decode_step(self.pool, self.slot_ids, self.q, self.k, self.v, self.a,
                              self.beta, self.o)
         gate_vec = self.w.gate == "keyvec"
@@ -113,12 +126,24 @@ class Harness:
             b, h = self.follow[n]
             j = (b, h) if idx_in_x is None else (n,)
             a = x_followed.a[j]
-            return self.ocfg.step_head(self.oslots[b], h, x_followed.q[j], x_followed.k[j],
-                                       x_followed.v[j], a if gate_vec else np.float32(a),
-                                       x_followed.beta[j])
+            a = a if gate_vec else np.float32(a)
+            o = self.ocfg.step_head(self.oslots[b], h, x_followed.q[j], x_followed.k[j],
+                                    x_followed.v[j], a, x_followed.beta[j])
+            e = 0.0
+            if self.shadow is not None:
+                o32 = oracle.step_f32(self.shadow[n], x_followed.q[j], x_followed.k[j],
+                                      x_followed.v[j], a, x_followed.beta[j], gate_vec)
+                e = float(np.max(np.abs(o - o32)) / max(float(np.max(np.abs(o32))), 1e-30))
+            return o, e
 
-        o_ref = list(self.exec.map(one, range(len(self.follow))))
-        o_gpu = self.o.cpu().numpy()
+        res = list(self.exec.map(one, range(len(self.follow))))
+        o_ref = [r[0] for r in res]
+        if self.shadow is not None:
+            self.shadow_err.append(max(r[1] for r in res))
+        if self.everything:
+            o_gpu = self.o.cpu().numpy()[self.fb, self.fh]
+        else:
+            o_gpu = self.o[self.fb_dev, self.fh_dev].cpu().numpy()
         self.t += 1
         return o_gpu, o_ref
 

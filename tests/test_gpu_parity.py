@@ -23,7 +23,7 @@ def _check_step(o_gpu, o_ref, follow, t, tag):
     from tests.parity import rel_err
     worst = 0.0
     for n, (b, h) in enumerate(follow):
-        e = rel_err(o_gpu[b, h], o_ref[n])
+        e = rel_err(o_gpu[n], o_ref[n])
         worst = max(worst, e)
         assert e <= O_TOL, f"{tag}: o mismatch at step {t}, unit (b={b}, h={h}): rel err {e:.3g}"
     return worst
@@ -80,31 +80,68 @@ def test_mixed_row_widths_d64():
     _run(w, 20, bits=bits, check_slots_every=5, tag="kda-mixed")
 
 
-def test_qwen_gdn_full_batch_sampled_units():
-    """Full B=64 x H=32 batch on the GPU, 48 followed units over all 256 steps."""
-    w = synth.WORKLOADS["qwen_gdn"]
-    rng = np.random.default_rng(2)
-    follow = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 48), rng.integers(0, w.H, 48))})
-    hs = _harness(w, follow=follow)
+def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None):
+    """Full batch on the GPU; n_units seeded (request, head) units (or the
+    given list) followed by the oracle over T steps (the others keep their
+    first inputs)."""
+    if follow is None:
+        rng = np.random.default_rng(seed)
+        follow = set()
+        while len(follow) < n_units:
+            follow.add((int(rng.integers(0, w.B)), int(rng.integers(0, w.H))))
+    follow = sorted(follow)
+    print(f"[{tag}] {w.name} layer {layer}: {len(follow)} followed units of B={w.B} x H={w.H}, "
+          f"T={T}", flush=True)
+    hs = _harness(w, layer=layer, follow=follow)
     try:
-        hs.load_full(0)  # every unit gets real inputs once; followed units get theirs each step
-        for t in range(w.T):
+        if track:
+            hs.track_fp32()
+        hs.init_state()
+        hs.load_full(0)
+        for t in range(T):
             x = hs.load_followed(t)
             o_gpu, o_ref = hs.step(x, idx_in_x=True)
-            _check_step(o_gpu, o_ref, hs.follow, t, "qwen-full")
-        assert not hs.compare_slots()
+            _check_step(o_gpu, o_ref, hs.follow, t, tag)
+            if (t + 1) % 256 == 0:
+                print(f"[{tag}] step {t + 1} ok", flush=True)
+        bad = hs.compare_slots()
+        assert not bad, f"{tag}: slot bytes differ after {T} steps: {bad[:4]}"
+        return hs
     finally:
         hs.close()
 
 
-def test_serving_gdn_all_units_short():
-    """B=512 x H=32 (16,384 states, 31 four-bit heads + 1 pivot head): all units, 3 steps."""
-    _run(synth.WORKLOADS["serving_gdn"], 3, tag="serving-all")
+def test_qwen_gdn_all_units_all_steps():
+    """B=64 x H=32, heads of 4/6/8 bits and an FP16 pivot head: every unit, all 256 steps."""
+    _run(synth.WORKLOADS["qwen_gdn"], 256, check_slots_every=64, tag="qwen-all")
 
 
-def test_kimi_kda_full_batch_all_units():
-    """B=256 x H=32 KDA with outlier start: every unit for 2 steps after the pack."""
-    _run(synth.WORKLOADS["kimi_kda"], 2, tag="kimi-all")
+def test_serving_gdn_all_units_16_steps():
+    """B=512 x H=32 (16,384 states, 31 four-bit heads + 1 pivot head): all units, 16 steps."""
+    _run(synth.WORKLOADS["serving_gdn"], 16, check_slots_every=8, tag="serving-all")
+
+
+def test_serving_gdn_sampled_units_all_2048_steps():
+    """Full serving batch, 64 followed units of layer 1 over all 2048 steps; the
+    distance of the quantized output from the unquantized fp32 recurrence is
+    tracked (reported, not a parity bar: it is the method's quantization error)."""
+    w = synth.WORKLOADS["serving_gdn"]
+    hs = _run_sampled(w, w.T, 64, seed=11, layer=1, track=True, tag="serving-long")
+    e = np.array(hs.shadow_err)
+    print(f"[serving-long] quantized vs fp32 output, max over units per step: "
+          f"median {np.median(e):.3g}, p90 {np.percentile(e, 90):.3g}, max {e.max():.3g}", flush=True)
+    assert np.isfinite(e).all()
+
+
+def test_kimi_kda_all_units_32_steps():
+    """B=256 x H=32 KDA (4-bit rows + 41 FP16 pivot rows), outlier start: every unit, 32 steps."""
+    _run(synth.WORKLOADS["kimi_kda"], 32, check_slots_every=16, tag="kimi-all")
+
+
+def test_kimi_kda_sampled_units_all_256_steps():
+    """Full KDA batch, 256 followed units over all 256 steps."""
+    w = synth.WORKLOADS["kimi_kda"]
+    _run_sampled(w, w.T, 256, seed=12, tag="kimi-long")
 
 
 def test_unpack_and_pack_match_oracle():
@@ -261,19 +298,17 @@ def test_windowed_unpack_mid_window():
         hs.close()
 
 
-def test_windowed_full_batch_sampled_units():
-    """B=512 x H=32 windowed KDA pool, 40 followed units over 3 windows."""
+@pytest.mark.parametrize("half", [0, 1])
+def test_windowed_all_units_two_windows(half):
+    """B=512 x H=32 windowed KDA pool: every unit over the first two windows
+    (each half of the requests in its own test, the whole batch on the GPU)."""
     w = synth.WORKLOADS["windowed_kda"]
-    rng = np.random.default_rng(6)
-    follow = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 40), rng.integers(0, w.H, 40))})
-    hs = _harness(w, follow=follow)
-    try:
-        hs.init_state()
-        hs.load_full(0)
-        for t in range(48):
-            x = hs.load_followed(t)
-            o_gpu, o_ref = hs.step(x, idx_in_x=True)
-            _check_step(o_gpu, o_ref, hs.follow, t, "win-full")
-        assert not hs.compare_slots()
-    finally:
-        hs.close()
+    reqs = range(half * w.B // 2, (half + 1) * w.B // 2)
+    _run_sampled(w, 32, 0, 0, follow=[(b, h) for b in reqs for h in range(w.H)],
+                 tag=f"win-all-{half}")
+
+
+def test_windowed_sampled_units_all_1024_steps():
+    """Full windowed batch, 256 followed units over all 1024 steps (64 window ends)."""
+    w = synth.WORKLOADS["windowed_kda"]
+    _run_sampled(w, w.T, 256, seed=13, tag="win-long")
