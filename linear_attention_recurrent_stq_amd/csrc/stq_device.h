@@ -1,7 +1,8 @@
 // Device helpers shared by the gfx950 kernels (stq_kernels.hip: per-step
 // decode, pack, unpack; stq_window.hip: windowed decode).  Internal.
 //
-// One workgroup owns one (request, head) state of d_k x d_v.  Thread t holds an
+// A workgroup steps one (request, head) state of d_k x d_v at a time (the step
+// kernel gives a workgroup two 4-bit heads of a request).  Thread t holds an
 // 8 x 8 block: key rows 8*rg .. 8*rg+7 and value columns 8*cg .. 8*cg+7, with
 // rg = t / (d_v/8) and cg = t % (d_v/8) (256 threads at d = 128, one wave at
 // d = 64).  That block is the unit of every memory access: in a row of b-bit

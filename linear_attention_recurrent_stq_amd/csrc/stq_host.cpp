@@ -22,7 +22,8 @@ struct stq_layout {
     std::vector<uint8_t> bits;          // H or H*d_k unit widths
     std::vector<stq::HeadDesc> heads;   // [H]
     std::vector<uint32_t> rows;         // [H*d_k] row table
-    std::vector<uint8_t> table;         // device image: heads then rows, 256-B padded
+    std::vector<uint32_t> groups;       // step-kernel head groups (h1 | h2 << 16)
+    std::vector<uint8_t> table;         // device image: heads, rows, groups; 256-B padded
     size_t slot_bytes = 0;
 };
 
@@ -85,6 +86,8 @@ stq::Args base_args(const stq_pool *p, int32_t B, const int32_t *ids) {
     a.slots = base + L->table.size();
     a.heads = reinterpret_cast<const stq::HeadDesc *>(base);
     a.rows = reinterpret_cast<const uint32_t *>(base + sizeof(stq::HeadDesc) * L->heads.size());
+    a.groups = a.rows + L->rows.size();
+    a.ngroups = (int32_t)L->groups.size();
     a.slot_bytes = L->slot_bytes;
     a.slot_ids = ids;
     a.B = B;
@@ -189,10 +192,27 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
         return fail(STQ_ERR_INVALID, "comps exceeds the quantized entries of a head");
     }
     L->slot_bytes = slot;
+    // Head groups of the step kernel: 4-bit heads in pairs (one workgroup
+    // steps both, fetching the second while computing the first), every
+    // other head alone.
+    int pending = -1;
+    for (int h = 0; h < H; ++h) {
+        if (L->heads[h].width != 4) {
+            L->groups.push_back((uint32_t)h | 0xffff0000u);
+        } else if (pending < 0) {
+            pending = h;
+        } else {
+            L->groups.push_back((uint32_t)pending | ((uint32_t)h << 16));
+            pending = -1;
+        }
+    }
+    if (pending >= 0) L->groups.push_back((uint32_t)pending | 0xffff0000u);
     const size_t hb = sizeof(stq::HeadDesc) * H, rb = sizeof(uint32_t) * (size_t)H * dk;
-    L->table.assign(up(hb + rb, 256), 0);
+    const size_t gb = sizeof(uint32_t) * L->groups.size();
+    L->table.assign(up(hb + rb + gb, 256), 0);
     std::memcpy(L->table.data(), L->heads.data(), hb);
     std::memcpy(L->table.data() + hb, L->rows.data(), rb);
+    std::memcpy(L->table.data() + hb + rb, L->groups.data(), gb);
     *out = L;
     return STQ_OK;
 }

@@ -50,6 +50,8 @@ struct Args {
     int32_t B, H, nslots;
     int32_t io_bf16, gate_vec, rs16, cs16;
     int32_t window, comps;
+    const uint32_t *groups;      // step kernel: [ngroups] head groups, h1 | h2 << 16
+    int32_t ngroups;             //   (h2 = 0xffff: a group of one head)
 };
 
 // Launchers (stq_kernels.hip).  Return the launch's hipError_t.  `mixed`: some

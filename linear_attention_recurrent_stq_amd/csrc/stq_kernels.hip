@@ -9,122 +9,203 @@ namespace {
 
 // ----------------------------------------------------------------- step
 
-template <int DK, int DV, int W>
+// The inputs of a 4-bit state that a workgroup fetches ahead of its compute:
+// for thread t, the code piece of each of its 8 rows, the inputs of key row t
+// (t < d_k) and of value column t (t < d_v).
+struct Pre4 {
+    float a, r, k, q;  // key row t: gate, row scale, key, query
+    float c, v;        // value column t: column scale, value
+    float beta;
+    uint32_t raw[8];
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void fetch4(const Args &A, const HeadDesc &hd, const uint8_t *R, size_t unit,
+                                       int t, int rg, int cg, Pre4 &p) {
+    const uint8_t *base = R + (uint32_t)(8 * rg * (DV / 2) + 4 * cg);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p.raw[r] = *reinterpret_cast<const uint32_t *>(base + r * (DV / 2));
+    p.beta = A.beta[unit];
+    if (t < DK) {
+        p.a = A.gate_vec ? A.a[unit * DK + t] : A.a[unit];
+        p.r = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[t])
+                     : reinterpret_cast<const float *>(R + hd.rs)[t];
+        p.k = load1(A.k, A.io_bf16, unit * DK + t);
+        p.q = load1(A.q, A.io_bf16, unit * DK + t);
+    }
+    if (t < DV) {
+        p.c = A.cs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+        p.v = load1(A.v, A.io_bf16, unit * DV + t);
+    }
+}
+
+// One state.  PRE: a 4-bit state whose inputs were fetched into p (W == 4);
+// otherwise the state's inputs are loaded here.
+template <int DK, int DV, int W, bool PRE>
 __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
-                                          Lds<DK, DV> &sm, int t, int rg, int cg) {
+                                          Lds<DK, DV> &sm, int t, int rg, int cg, const Pre4 &p) {
+    static_assert(!PRE || W == 4, "prefetch is for 4-bit heads");
     const bool quant = has_quant<W>(hd);
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
     uint4 raw[8];
+    if (PRE) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+        for (int r = 0; r < 8; ++r) raw[r] = make_uint4(p.raw[r], 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+    }
 
     // per key row and per value column constants, computed once per state
-    const float beta = A.beta[unit];
-    float vv = 0.0f;
-    if (t < DK) {
-        const int i = t;
-        const int w = width_of<W>(A, hd, i);
-        const float a = A.gate_vec ? A.a[unit * DK + i] : A.a[unit];
-        float ri = 0.0f;
-        if (quant && w != 16)
-            ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
-                        : reinterpret_cast<const float *>(R + hd.rs)[i];
-        const float g = a * ri;
-        sm.g[i] = g;
-        sm.g16[i] = g * 0.0625f;
-        sm.nog[i] = w != 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
-        sm.af[i] = a;
-        sm.kf[i] = load1(A.k, A.io_bf16, unit * DK + i);
-        sm.qf[i] = load1(A.q, A.io_bf16, unit * DK + i);
-    }
-    if (t < DV) {
-        sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
-        vv = load1(A.v, A.io_bf16, unit * DV + t);
-    }
-    __syncthreads();
-
-    float kk[8], qq[8], cc[8];
-    lds_read8(&sm.kf[8 * rg], kk, 0);
-    lds_read8(&sm.qf[8 * rg], qq, 0);
-    lds_read8(&sm.cf[8 * cg], cc, 0);
-
-    // decay + dequantize: A_ij
-    float x[8][8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int i = 8 * rg + r;
-        const int w = rw.w[r];
-        if (w == 16) {
-            const float a = sm.af[i];
-            const uint32_t hv[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                x[r][2 * c] = a * f16v(hv[c]);
-                x[r][2 * c + 1] = a * f16v(hv[c] >> 16);
-            }
-        } else {
-            dequant_row(raw[r], w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * cc[c];
+    float beta, vv = 0.0f;
+    if (PRE) {
+        beta = p.beta;
+        if (t < DK) {
+            const float g = p.a * p.r;
+            sm.g[t] = g;
+            sm.g16[t] = g * 0.0625f;
+            sm.nog[t] = -8.0f * g;
+            sm.af[t] = p.a;
+            sm.kf[t] = p.k;
+            sm.qf[t] = p.q;
+        }
+        if (t < DV) {
+            sm.cf[t] = p.c;
+            vv = p.v;
+        }
+    } else {
+        beta = A.beta[unit];
+        if (t < DK) {
+            const int i = t;
+            const int w = width_of<W>(A, hd, i);
+            const float a = A.gate_vec ? A.a[unit * DK + i] : A.a[unit];
+            float ri = 0.0f;
+            if (quant && w != 16)
+                ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
+                            : reinterpret_cast<const float *>(R + hd.rs)[i];
+            const float g = a * ri;
+            sm.g[i] = g;
+            sm.g16[i] = g * 0.0625f;
+            sm.nog[i] = w != 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
+            sm.af[i] = a;
+            sm.kf[i] = load1(A.k, A.io_bf16, unit * DK + i);
+            sm.qf[i] = load1(A.q, A.io_bf16, unit * DK + i);
+        }
+        if (t < DV) {
+            sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+            vv = load1(A.v, A.io_bf16, unit * DV + t);
         }
     }
-
-    // w = (a.S) k : column partial sums over the thread's 8 rows
+    __syncthreads();
+    // decay + dequantize: A_ij, row by row, with the w = (a.S) k column
+    // partial sums over the thread's 8 rows accumulated as the rows come in.
+    // Vectors are read from LDS where they are used, so that none of them is
+    // held across a barrier.
+    float x[8][8];
+    {
+        float kk[8], cc[8], s[8];
+        lds_read8(&sm.kf[8 * rg], kk, 0);
+        lds_read8(&sm.cf[8 * cg], cc, 0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        float s = x[0][c] * kk[0];
+        for (int r = 0; r < 8; ++r) {
+            const int i = 8 * rg + r;
+            const int w = rw.w[r];
+            if (w == 16) {
+                const float a = sm.af[i];
+                const uint32_t hv[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
 #pragma unroll
-        for (int r = 1; r < 8; ++r) s = fma_(x[r][c], kk[r], s);
-        sm.colp[c][t] = s;
+                for (int c = 0; c < 4; ++c) {
+                    x[r][2 * c] = a * f16v(hv[c]);
+                    x[r][2 * c + 1] = a * f16v(hv[c] >> 16);
+                }
+            } else {
+                dequant_row(raw[r], w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * cc[c];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s[c] = r == 0 ? x[0][c] * kk[0] : fma_(x[r][c], kk[r], s[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sm.colp[c][t] = s[c];
     }
     __syncthreads();
     if (t < DV) sm.u[t] = beta * (vv - col_sum<DK, DV>(sm, t));
     __syncthreads();
-    float uu[8];
-    lds_read8(&sm.u[8 * cg], uu, 0);
 
-    // rank-1 write and o = S_new q partial sums
+    // rank-1 write, then o = S_new q partial sums
+    {
+        float kk[8], uu[8];
+        lds_read8(&sm.kf[8 * rg], kk, 0);
+        lds_read8(&sm.u[8 * cg], uu, 0);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+        for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) x[r][c] = fma_(kk[r], uu[c], x[r][c]);
+            for (int c = 0; c < 8; ++c) x[r][c] = fma_(kk[r], uu[c], x[r][c]);
+    }
+    {
+        float qq[8];
+        lds_read8(&sm.qf[8 * rg], qq, 0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        float s = x[0][c] * qq[0];
+        for (int c = 0; c < 8; ++c) {
+            float s = x[0][c] * qq[0];
 #pragma unroll
-        for (int r = 1; r < 8; ++r) s = fma_(x[r][c], qq[r], s);
-        sm.colp[c][t] = s;
+            for (int r = 1; r < 8; ++r) s = fma_(x[r][c], qq[r], s);
+            sm.colp[c][t] = s;
+        }
     }
     requant_store<DK, DV, W>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
 }
 
-// One workgroup per (request, head) state.  MIXED: some head of the layout
-// has rows of different widths (KDA); without it the per-row width path is not
-// compiled, which saves registers.
+
+// Workgroup g steps the states of head group g % ngroups of request
+// g / ngroups.  A group is one head, or two 4-bit heads: then the second
+// state's inputs are fetched before the first is computed, so their latency
+// is hidden behind that compute (workgroup barriers wait only for LDS
+// traffic).  MIXED: some head of the layout has rows of different widths
+// (KDA); without it the per-row width path is not compiled.
 template <int DK, int DV, bool MIXED>
 __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
     constexpr int CG = DV / 8;
     __shared__ Lds<DK, DV> sm;
-    const size_t unit = blockIdx.x;
-    const int b = (int)(unit / (size_t)A.H);
-    const int h = (int)(unit - (size_t)b * A.H);
+    const int ng = A.ngroups;
+    const int b = (int)(blockIdx.x / (uint32_t)ng);
+    const int gi = (int)(blockIdx.x - (uint32_t)b * ng);
+    const uint32_t grp = A.groups[gi];
+    const int h1 = (int)(grp & 0xffffu), h2 = (int)(grp >> 16);
     const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
+    const size_t u1 = (size_t)b * A.H + h1;
     const int slot = A.slot_ids[b];
     if (slot < 0 || slot >= A.nslots) {
-        // an invalid slot id touches no state; its output is NaN
-        if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
+        // an invalid slot id touches no state; its outputs are NaN
+        if (t < DV) {
+            A.o[u1 * DV + t] = __builtin_nanf("");
+            if (h2 != 0xffff) A.o[((size_t)b * A.H + h2) * DV + t] = __builtin_nanf("");
+        }
         return;
     }
-    const HeadDesc &hd = A.heads[h];
-    uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
-    switch (hd.width) {
-        case 4: step_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 6: step_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 8: step_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 16: step_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+    uint8_t *S = A.slots + (size_t)slot * A.slot_bytes;
+    const HeadDesc &hd1 = A.heads[h1];
+    if (h2 != 0xffff) {
+        const HeadDesc &hd2 = A.heads[h2];
+        const size_t u2 = (size_t)b * A.H + h2;
+        Pre4 p1, p2;
+        fetch4<DK, DV>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
+        fetch4<DK, DV>(A, hd2, S + hd2.off, u2, t, rg, cg, p2);
+        step_tile<DK, DV, 4, true>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
+        step_tile<DK, DV, 4, true>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
+        return;
+    }
+    uint8_t *R = S + hd1.off;
+    Pre4 none;
+    switch (hd1.width) {
+        case 4: step_tile<DK, DV, 4, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 6: step_tile<DK, DV, 6, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 8: step_tile<DK, DV, 8, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 16: step_tile<DK, DV, 16, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         default:
-            if (MIXED) step_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            if (MIXED) step_tile<DK, DV, 0, false>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
     }
 }
@@ -255,11 +336,18 @@ hipError_t launch_dims(void (*k)(Args), const Args &a, hipStream_t s) {
     if (dk == 64 && dv == 128) return launch_dims<64, 128>(KERNEL<64, 128>, a, s);    \
     return hipErrorInvalidValue;
 
+template <int DK, int DV, bool MIXED>
+hipError_t launch_step_dims(const Args &a, hipStream_t s) {
+    if (a.B == 0) return hipSuccess;
+    void (*k)(Args) = k_step<DK, DV, MIXED>;
+    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * a.ngroups)), dim3(DK * DV / 64), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
 #define STQ_STEP(DK_, DV_)                                                                      \
     if (dk == DK_ && dv == DV_)                                                                 \
-        return mixed ? launch_dims<DK_, DV_>(k_step<DK_, DV_, true>, a, s)                      \
-                     : launch_dims<DK_, DV_>(k_step<DK_, DV_, false>, a, s);
+        return mixed ? launch_step_dims<DK_, DV_, true>(a, s) : launch_step_dims<DK_, DV_, false>(a, s);
     STQ_STEP(128, 128)
     STQ_STEP(64, 64)
     STQ_STEP(128, 64)

@@ -53,13 +53,36 @@ def test_layout_mixed_rows_matches_oracle(stq, ora):
             assert L.head(h) == (o.head_layout(h)["base"], o.head_layout(h)["bytes"])
 
 
+def _header_bytes(H, dk, widths):
+    """Device table: head descriptors (64 B each), the row table (4 B per key
+    row), then the step kernel's head groups (4 B each: 4-bit heads in pairs,
+    every other head alone), padded to 256 B."""
+    four = sum(1 for x in widths if x == 4)
+    groups = (four + 1) // 2 + sum(1 for x in widths if x != 4)
+    n = 64 * H + 4 * H * dk + 4 * groups
+    return (n + 255) // 256 * 256
+
+
 def test_pool_size_query_without_device(stq):
     w = synth.WORKLOADS["serving_gdn"]
-    L = stq.Layout.from_workload(w, synth.unit_bits(w))
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
     q = stq.StqPool()
     assert stq.library().stq_alloc_pool(L.handle, 512, None, 0, None, C.byref(q)) == stq.STQ_OK
     assert q.bytes == L.header_bytes + 512 * 302592
-    assert L.header_bytes % 256 == 0 and L.header_bytes >= 64 * 32 + 4 * 32 * 128
+    assert L.header_bytes == _header_bytes(32, 128, bits)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_header_holds_the_head_groups(stq, name):
+    w = synth.WORKLOADS[name]
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    # per-key-row layouts have no uniform 4-bit heads unless every row is 4-bit
+    per_head = bits if w.unit == "head" else [
+        int(bits[h * w.dk]) if (bits[h * w.dk:(h + 1) * w.dk] == bits[h * w.dk]).all() else 0
+        for h in range(w.H)]
+    assert L.header_bytes == _header_bytes(w.H, w.dk, per_head)
 
 
 @pytest.mark.parametrize("field,value,status", [
