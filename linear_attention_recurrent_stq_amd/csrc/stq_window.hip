@@ -30,20 +30,29 @@ constexpr int kWMax = 16;     // window length supported by the LDS staging
 constexpr int kKMax = 1024;   // compensation entries
 constexpr int kCandMax = 1024;  // top-K candidates ranked exactly
 
+// LDS of the window-end, pack and unpack kernels.
 template <int DK, int DV>
 struct LdsW {
     Lds<DK, DV> b;            // per-step arrays (partials, row/column constants, 1/c', 1/r')
-    float kr[DK], qr[DK];     // k and q as fp32
-    float gn[DK];             // cumulative gate after this step
-    float ckp[kWMax][DK / 8], cqp[kWMax][DK / 8];  // csum block partials of kap_m . k, kap_m . q
-    float ck[kWMax], cq[kWMax];
-    float kst[kWMax][DK];     // decayed delta keys (window end)
+    float gn[DK];             // cumulative gate
+    float kst[kWMax][DK];     // decayed delta keys
     float ust[kWMax][DV];     // delta values
     uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
     float cvl[kKMax];         // compensation value
     uint32_t ckey[kCandMax];  // candidate keys
     int red[2][8];            // block reductions
     uint32_t bc[4];           // broadcasts
+};
+
+// LDS of the in-window step; the compensation entries follow in dynamic LDS
+// ([K] index, [K] value).
+template <int DK, int DV>
+struct LdsWin {
+    Lds<DK, DV> b;
+    float kr[DK], qr[DK];     // k and q as fp32
+    float ckp[kWMax][DK / 8], cqp[kWMax][DK / 8];  // csum block partials of kap_m . k, kap_m . q
+    float ck[kWMax], cq[kWMax];
+    uint32_t cstart[DV + 1];  // entries of column j: cstart[j] .. cstart[j+1]-1
 };
 
 // Block-wide sum of one int per thread (alternating buffers: one barrier).
@@ -148,20 +157,27 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                     }
                 }
             __syncthreads();
-            // 3) exact rank of every candidate; the K-th one is (thr, pk)
-            for (int e = t; e < total; e += NT) {
-                const float v = reinterpret_cast<const float *>(sm.ckey)[e];
-                const uint32_t p = sm.cix[e];
-                int rank2 = 0;
-                for (int f = 0; f < total; ++f) {
-                    const float v2 = reinterpret_cast<const float *>(sm.ckey)[f];
-                    rank2 += (v2 > v) || (v2 == v && sm.cix[f] < p);
-                }
-                if (rank2 == K - 1) { sm.bc[2] = __float_as_uint(v); sm.bc[3] = p; }
+            // 3) the K-th candidate in the order (|M| descending, p ascending):
+            //    bit-serial search of its |M| pattern, then of its p among the ties
+            uint32_t P = 0;
+            for (int bit = 30; bit >= 0; --bit) {
+                const uint32_t cand = P | (1u << bit);
+                int m = 0;
+                for (int e = t; e < total; e += NT) m += sm.ckey[e] >= cand;
+                if (block_sum<NT>(m, sm.red, phase) >= K) P = cand;
             }
-            __syncthreads();
-            thr = __uint_as_float(sm.bc[2]);
-            pk = sm.bc[3];
+            int above = 0;
+            for (int e = t; e < total; e += NT) above += sm.ckey[e] > P;
+            const int need = K - block_sum<NT>(above, sm.red, phase);
+            uint32_t X = 0;
+            for (int bit = 15; bit >= 0; --bit) {
+                const uint32_t cand = X | (1u << bit);
+                int m = 0;
+                for (int e = t; e < total; e += NT) m += (sm.ckey[e] == P) & (sm.cix[e] < cand);
+                if (block_sum<NT>(m, sm.red, phase) < need) X = cand;
+            }
+            thr = __uint_as_float(P);
+            pk = X;
             exact = true;
         }
     }
@@ -230,7 +246,7 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
 // Base B of one row piece: RN(RN(n r) c) for a quantized row (n r is exact),
 // the stored fp16 values for a pivot row.  No compensation entries.
 template <int DK, int DV>
-__device__ __forceinline__ void base_row(int w, uint4 raw, const LdsW<DK, DV> &sm, int i,
+__device__ __forceinline__ void base_row(int w, uint4 raw, const Lds<DK, DV> &sm, int i,
                                          const float (&cc)[8], float (&x)[8]) {
     if (w == 16) {
         const uint32_t hv[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -240,14 +256,14 @@ __device__ __forceinline__ void base_row(int w, uint4 raw, const LdsW<DK, DV> &s
             x[2 * c + 1] = f16v(hv[c] >> 16);
         }
     } else {
-        dequant_row(raw, w, sm.b.g[i], sm.b.g16[i], sm.b.nog[i], x);
+        dequant_row(raw, w, sm.g[i], sm.g16[i], sm.nog[i], x);
 #pragma unroll
         for (int c = 0; c < 8; ++c) x[c] = x[c] * cc[c];
     }
 }
 
 template <int DK, int DV>
-__device__ __forceinline__ void base_block(const Rows &rw, const uint4 (&raw)[8], const LdsW<DK, DV> &sm,
+__device__ __forceinline__ void base_block(const Rows &rw, const uint4 (&raw)[8], const Lds<DK, DV> &sm,
                                            int rg, const float (&cc)[8], float (&x)[8][8]) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) base_row<DK, DV>(rw.w[r], raw[r], sm, 8 * rg + r, cc, x[r]);
@@ -257,7 +273,7 @@ __device__ __forceinline__ void base_block(const Rows &rw, const uint4 (&raw)[8]
 // r/16 in g16, -2^(w-1) r in nog; column scales in cf).
 template <int DK, int DV, int W>
 __device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd, const uint8_t *R,
-                                               LdsW<DK, DV> &sm, int t) {
+                                               Lds<DK, DV> &sm, int t) {
     const bool quant = has_quant<W>(hd);
     if (t < DK) {
         const int w = width_of<W>(A, hd, t);
@@ -265,17 +281,18 @@ __device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd
         if (quant && w != 16)
             ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[t])
                         : reinterpret_cast<const float *>(R + hd.rs)[t];
-        sm.b.g[t] = ri;
-        sm.b.g16[t] = ri * 0.0625f;
-        sm.b.nog[t] = w != 16 ? -(float)(1 << (w - 1)) * ri : 0.0f;
+        sm.g[t] = ri;
+        sm.g16[t] = ri * 0.0625f;
+        sm.nog[t] = w != 16 ? -(float)(1 << (w - 1)) * ri : 0.0f;
     }
     if (t < DV)
-        sm.b.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+        sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
 }
 
 template <int DK, int DV, int W>
 __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
-                                         LdsW<DK, DV> &sm, int t, int rg, int cg) {
+                                         LdsWin<DK, DV> &sm, uint32_t *cix, float *cvl, int t, int rg,
+                                         int cg) {
     constexpr int NT = DK * DV / 64, RG = DK / 8;
     const int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
     const int W_ = A.window;
@@ -294,8 +311,27 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     float *du = reinterpret_cast<float *>(R + hd.du);
     float *dkap = reinterpret_cast<float *>(R + hd.dkap);
 
-    // per key row / value column constants and the stored delta values
-    base_constants<DK, DV, W>(A, hd, R, sm, t);
+    // Loads issued before the first barrier: the stored delta values of
+    // column t (read only by thread t) and the first (delta, 8-row block)
+    // of delta keys that this thread decays.
+    float um[kWMax];
+    if (t < DV) {
+#pragma unroll
+        for (int m = 0; m < kWMax; ++m) um[m] = m < n ? du[(size_t)m * DV + t] : 0.0f;
+    }
+    float kap0[8];
+    {
+        const int m0 = t / RG, i0 = 8 * (t - m0 * RG);
+        if (m0 < n) {
+            const float4 *p = reinterpret_cast<const float4 *>(dkap + (size_t)m0 * DK + i0);
+            const float4 a0 = p[0], a1 = p[1];
+            kap0[0] = a0.x; kap0[1] = a0.y; kap0[2] = a0.z; kap0[3] = a0.w;
+            kap0[4] = a1.x; kap0[5] = a1.y; kap0[6] = a1.z; kap0[7] = a1.w;
+        }
+    }
+
+    // per key row / value column constants
+    base_constants<DK, DV, W>(A, hd, R, sm.b, t);
     const float beta = A.beta[unit];
     float vv = 0.0f;
     if (t < DK) {
@@ -306,20 +342,28 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         sm.b.af[t] = a;
         sm.kr[t] = k;
         sm.qr[t] = q;
-        sm.gn[t] = g;
         sm.b.kf[t] = g * k;
         sm.b.qf[t] = g * q;
         gmem[t] = g;
     }
-    if (t < DV) {
-        vv = load1(A.v, A.io_bf16, unit * DV + t);
-        for (int m = 0; m < n; ++m) sm.ust[m][t] = du[(size_t)m * DV + t];
-    }
+    if (t < DV) vv = load1(A.v, A.io_bf16, unit * DV + t);
     for (int e = t; e < K; e += NT) {
-        sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
-        sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+        cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
+        cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
     }
     __syncthreads();
+
+    // column ranges of the entries (sorted by p = j*d_k + i)
+    if (K == 0) {
+        for (int j = t; j <= DV; j += NT) sm.cstart[j] = 0;
+    }
+    for (int e = t; e < K; e += NT) {
+        const int j = (int)(cix[e] / DK);
+        const int jp = e > 0 ? (int)(cix[e - 1] / DK) : -1;
+        for (int jj = jp + 1; jj <= j; ++jj) sm.cstart[jj] = e;
+        if (e == K - 1)
+            for (int jj = j + 1; jj <= DV; ++jj) sm.cstart[jj] = K;
+    }
 
     // delta keys: decay, store back, block partials of kap . k and kap . q
     for (int pr = t; pr < (n + 1) * RG; pr += NT) {
@@ -327,9 +371,14 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         float kap[8];
         if (m < n) {
             float4 *p = reinterpret_cast<float4 *>(dkap + (size_t)m * DK + i0);
-            const float4 a0 = p[0], a1 = p[1];
-            kap[0] = a0.x; kap[1] = a0.y; kap[2] = a0.z; kap[3] = a0.w;
-            kap[4] = a1.x; kap[5] = a1.y; kap[6] = a1.z; kap[7] = a1.w;
+            if (pr == t) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) kap[r] = kap0[r];
+            } else {
+                const float4 a0 = p[0], a1 = p[1];
+                kap[0] = a0.x; kap[1] = a0.y; kap[2] = a0.z; kap[3] = a0.w;
+                kap[4] = a1.x; kap[5] = a1.y; kap[6] = a1.z; kap[7] = a1.w;
+            }
 #pragma unroll
             for (int r = 0; r < 8; ++r) kap[r] = kap[r] * sm.b.af[i0 + r];
             p[0] = make_float4(kap[0], kap[1], kap[2], kap[3]);
@@ -354,7 +403,7 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     lds_read8(&sm.b.kf[8 * rg], kk, 0);
     lds_read8(&sm.b.qf[8 * rg], qq, 0);
     float x[8][8];
-    base_block<DK, DV>(rw, raw, sm, rg, cc, x);
+    base_block<DK, DV>(rw, raw, sm.b, rg, cc, x);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         float s = x[0][c] * kk[0], s2 = x[0][c] * qq[0];
@@ -390,16 +439,19 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
 
     if (t < DV) {
         const int j = t;
-        const int lo = lower_bound(sm.cix, K, (uint32_t)(j * DK));
-        const int hi = lower_bound(sm.cix, K, (uint32_t)((j + 1) * DK));
+        const int lo = (int)sm.cstart[j], hi = (int)sm.cstart[j + 1];
         float w = w0;
-        for (int e = lo; e < hi; ++e) w = fma_(sm.cvl[e], sm.b.kf[sm.cix[e] - j * DK], w);
-        for (int m = 0; m < n; ++m) w = fma_(sm.ust[m][j], sm.ck[m], w);
+        for (int e = lo; e < hi; ++e) w = fma_(cvl[e], sm.b.kf[cix[e] - j * DK], w);
+#pragma unroll
+        for (int m = 0; m < kWMax; ++m)
+            if (m < n) w = fma_(um[m], sm.ck[m], w);
         const float u = beta * (vv - w);
         du[(size_t)n * DV + j] = u;
         float o = o0;
-        for (int e = lo; e < hi; ++e) o = fma_(sm.cvl[e], sm.b.qf[sm.cix[e] - j * DK], o);
-        for (int m = 0; m < n; ++m) o = fma_(sm.ust[m][j], sm.cq[m], o);
+        for (int e = lo; e < hi; ++e) o = fma_(cvl[e], sm.b.qf[cix[e] - j * DK], o);
+#pragma unroll
+        for (int m = 0; m < kWMax; ++m)
+            if (m < n) o = fma_(um[m], sm.cq[m], o);
         o = fma_(u, sm.cq[n], o);
         A.o[unit * DV + j] = o;
     }
@@ -425,7 +477,7 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
     float *gmem = reinterpret_cast<float *>(R + hd.g);
     const float *du = reinterpret_cast<const float *>(R + hd.du);
     const float *dkap = reinterpret_cast<const float *>(R + hd.dkap);
-    base_constants<DK, DV, W>(A, hd, R, sm, t);
+    base_constants<DK, DV, W>(A, hd, R, sm.b, t);
     for (int e = t; e < n * DK; e += NT) sm.kst[e / DK][e % DK] = dkap[e];
     for (int e = t; e < n * DV; e += NT) sm.ust[e / DV][e % DV] = du[e];
     if (t < DK) sm.gn[t] = gmem[t];
@@ -473,7 +525,7 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         float B[8];
-        base_row<DK, DV>(rw.w[r], raw[r], sm, 8 * rg + r, cc, B);
+        base_row<DK, DV>(rw.w[r], raw[r], sm.b, 8 * rg + r, cc, B);
         const uint32_t dr = (uint32_t)(done >> (8 * r)) & 0xffu;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -513,7 +565,10 @@ __global__ void __launch_bounds__(DK * DV / 64) k_win_end(Args A) {
 template <int DK, int DV, bool MIXED>
 __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     constexpr int CG = DV / 8;
-    __shared__ LdsW<DK, DV> sm;
+    __shared__ LdsWin<DK, DV> sm;
+    extern __shared__ uint32_t win_entries[];  // [K] index, then [K] value
+    uint32_t *cix = win_entries;
+    float *cvl = reinterpret_cast<float *>(win_entries + A.comps);
     const size_t unit = blockIdx.x;
     const int b = (int)(unit / (size_t)A.H);
     const int h = (int)(unit - (size_t)b * A.H);
@@ -526,12 +581,12 @@ __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     switch (hd.width) {
-        case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
-        case 16: win_tile<DK, DV, 16>(A, hd, R, unit, sm, t, rg, cg); break;
+        case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
+        case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
+        case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
+        case 16: win_tile<DK, DV, 16>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
         default:
-            if (MIXED) win_tile<DK, DV, 0>(A, hd, R, unit, sm, t, rg, cg);
+            if (MIXED) win_tile<DK, DV, 0>(A, hd, R, unit, sm, cix, cvl, t, rg, cg);
             break;
     }
 }
@@ -616,7 +671,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack_win(Args A) {
     uint4 raw[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
-    base_constants<DK, DV, 0>(A, hd, R, sm, t);
+    base_constants<DK, DV, 0>(A, hd, R, sm.b, t);
     for (int e = t; e < K; e += DK * DV / 64) {
         sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
         sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
@@ -625,7 +680,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack_win(Args A) {
     float cc[8];
     lds_read8(&sm.b.cf[8 * cg], cc, 0);
     float x[8][8];
-    base_block<DK, DV>(rw, raw, sm, rg, cc, x);
+    base_block<DK, DV>(rw, raw, sm.b, rg, cc, x);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const uint32_t p0 = (uint32_t)((8 * cg + c) * DK + 8 * rg);
@@ -662,37 +717,38 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack_win(Args A) {
 }
 
 template <int DK, int DV>
-hipError_t launch_grid(void (*k)(Args), const Args &a, hipStream_t s) {
+hipError_t launch_grid(void (*k)(Args), const Args &a, hipStream_t s, size_t lds = 0) {
     if (a.B == 0) return hipSuccess;
-    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * a.H)), dim3(DK * DV / 64), 0, s, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * a.H)), dim3(DK * DV / 64), lds, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-#define STQ_WIN_DISPATCH(KERNEL)                                                               \
+#define STQ_WIN_DISPATCH(KERNEL, LDS)                                                          \
     if (dk == 128 && dv == 128)                                                               \
-        return mixed ? launch_grid<128, 128>(KERNEL<128, 128, true>, a, s)                     \
-                     : launch_grid<128, 128>(KERNEL<128, 128, false>, a, s);                   \
+        return mixed ? launch_grid<128, 128>(KERNEL<128, 128, true>, a, s, LDS)                \
+                     : launch_grid<128, 128>(KERNEL<128, 128, false>, a, s, LDS);              \
     if (dk == 64 && dv == 64)                                                                 \
-        return mixed ? launch_grid<64, 64>(KERNEL<64, 64, true>, a, s)                         \
-                     : launch_grid<64, 64>(KERNEL<64, 64, false>, a, s);                       \
+        return mixed ? launch_grid<64, 64>(KERNEL<64, 64, true>, a, s, LDS)                    \
+                     : launch_grid<64, 64>(KERNEL<64, 64, false>, a, s, LDS);                  \
     if (dk == 128 && dv == 64)                                                                \
-        return mixed ? launch_grid<128, 64>(KERNEL<128, 64, true>, a, s)                       \
-                     : launch_grid<128, 64>(KERNEL<128, 64, false>, a, s);                     \
+        return mixed ? launch_grid<128, 64>(KERNEL<128, 64, true>, a, s, LDS)                  \
+                     : launch_grid<128, 64>(KERNEL<128, 64, false>, a, s, LDS);                \
     if (dk == 64 && dv == 128)                                                                \
-        return mixed ? launch_grid<64, 128>(KERNEL<64, 128, true>, a, s)                       \
-                     : launch_grid<64, 128>(KERNEL<64, 128, false>, a, s);                     \
+        return mixed ? launch_grid<64, 128>(KERNEL<64, 128, true>, a, s, LDS)                  \
+                     : launch_grid<64, 128>(KERNEL<64, 128, false>, a, s, LDS);                \
     return hipErrorInvalidValue;
 
 hipError_t launch_step_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
-    const hipError_t e = [&]() -> hipError_t { STQ_WIN_DISPATCH(k_win) }();
+    const size_t entries = (size_t)a.comps * 8;  // index + value per compensation entry
+    const hipError_t e = [&]() -> hipError_t { STQ_WIN_DISPATCH(k_win, entries) }();
     if (e != hipSuccess) return e;
-    STQ_WIN_DISPATCH(k_win_end)
+    STQ_WIN_DISPATCH(k_win_end, 0)
 }
 
 hipError_t launch_pack_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
-    STQ_WIN_DISPATCH(k_pack_win)
+    STQ_WIN_DISPATCH(k_pack_win, 0)
 }
 
 hipError_t launch_unpack_win(const Args &a, int dk, int dv, hipStream_t s) {
