@@ -44,14 +44,15 @@ struct LdsW {
     uint32_t bc[4];           // broadcasts
 };
 
-// LDS of the in-window step; the compensation entries follow in dynamic LDS
-// ([K] index, [K] value).
+// LDS of the in-window step; the compensation entries follow in dynamic LDS:
+// [K] index, [K] value, and per entry the gated key and query of its row.
 template <int DK, int DV>
 struct LdsWin {
     Lds<DK, DV> b;
     float kr[DK], qr[DK];     // k and q as fp32
     float ckp[kWMax][DK / 8], cqp[kWMax][DK / 8];  // csum block partials of kap_m . k, kap_m . q
-    float ck[kWMax], cq[kWMax];
+    alignas(16) float ck[kWMax];
+    alignas(16) float cq[kWMax];
     uint32_t cstart[DV + 1];  // entries of column j: cstart[j] .. cstart[j+1]-1
 };
 
@@ -69,6 +70,24 @@ __device__ __forceinline__ int block_sum(int v, int (&red)[2][8], int &phase) {
     for (int w = 0; w < NW; ++w) s += red[phase][w];
     phase ^= 1;
     return s;
+}
+
+// Block-wide sum of a small non-negative count per thread (< 2^BITS), from
+// one wave ballot per bit (alternating buffers: one barrier).
+template <int NT, int BITS>
+__device__ __forceinline__ int block_count(int v, int (&red)[2][8], int &phase) {
+    constexpr int NW = NT / 64;
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) s += (int)__popcll(__ballot((v >> k) & 1)) << k;
+    const int t = threadIdx.x;
+    if ((t & 63) == 0) red[phase][t >> 6] = s;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += red[phase][w];
+    phase ^= 1;
+    return tot;
 }
 
 // First index e in [0, n) with a[e] >= x (a sorted ascending).
@@ -136,8 +155,10 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
             rank += (o > tmax) || (o == tmax && s2 < t);
         }
         if (rank == K - 1) sm.bc[0] = __float_as_uint(tmax);
+        if (rank == 0) sm.bc[2] = __float_as_uint(tmax);
         __syncthreads();
         const float t0 = __uint_as_float(sm.bc[0]);
+        const uint32_t kmax = sm.bc[2];
         // 2) compact the candidates |M| >= t0 into LDS when they are few
         const int mine = t0 >= 0.0f ? count_ge(x, rw, t0) : 0;
         const int total = block_sum<NT>(mine, sm.red, phase);
@@ -158,23 +179,29 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                 }
             __syncthreads();
             // 3) the K-th candidate in the order (|M| descending, p ascending):
-            //    bit-serial search of its |M| pattern, then of its p among the ties
-            uint32_t P = 0;
-            for (int bit = 30; bit >= 0; --bit) {
+            //    bit-serial search of its |M| pattern (every candidate lies in
+            //    [t0, largest], so the bits above the highest one where those
+            //    two differ are known), then of its p among the ties
+            constexpr int CB = kCandMax / NT >= 16 ? 5 : kCandMax / NT >= 8 ? 4 : 3;  // bits of a count
+            constexpr int PB = DK * DV > 8192 ? 14 : DK * DV > 4096 ? 13 : 12;           // bits of p
+            const uint32_t lo = __float_as_uint(t0);
+            const int top = (lo ^ kmax) ? 31 - __builtin_clz(lo ^ kmax) : -1;
+            uint32_t P = top >= 0 ? lo & ~((2u << top) - 1u) : lo;
+            for (int bit = top; bit >= 0; --bit) {
                 const uint32_t cand = P | (1u << bit);
                 int m = 0;
                 for (int e = t; e < total; e += NT) m += sm.ckey[e] >= cand;
-                if (block_sum<NT>(m, sm.red, phase) >= K) P = cand;
+                if (block_count<NT, CB>(m, sm.red, phase) >= K) P = cand;
             }
             int above = 0;
             for (int e = t; e < total; e += NT) above += sm.ckey[e] > P;
-            const int need = K - block_sum<NT>(above, sm.red, phase);
+            const int need = K - block_count<NT, CB>(above, sm.red, phase);
             uint32_t X = 0;
-            for (int bit = 15; bit >= 0; --bit) {
+            for (int bit = PB - 1; bit >= 0; --bit) {
                 const uint32_t cand = X | (1u << bit);
                 int m = 0;
                 for (int e = t; e < total; e += NT) m += (sm.ckey[e] == P) & (sm.cix[e] < cand);
-                if (block_sum<NT>(m, sm.red, phase) < need) X = cand;
+                if (block_count<NT, CB>(m, sm.red, phase) < need) X = cand;
             }
             thr = __uint_as_float(P);
             pk = X;
@@ -291,8 +318,8 @@ __device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd
 
 template <int DK, int DV, int W>
 __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
-                                         LdsWin<DK, DV> &sm, uint32_t *cix, float *cvl, int t, int rg,
-                                         int cg) {
+                                         LdsWin<DK, DV> &sm, uint32_t *cix, float *cvl, float *kge, float *qge,
+                                         int t, int rg, int cg) {
     constexpr int NT = DK * DV / 64, RG = DK / 8;
     const int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
     const int W_ = A.window;
@@ -353,12 +380,16 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     }
     __syncthreads();
 
-    // column ranges of the entries (sorted by p = j*d_k + i)
+    // column ranges of the entries (sorted by p = j*d_k + i), and each
+    // entry's gated key and query (the operands of its fma in w and o)
     if (K == 0) {
         for (int j = t; j <= DV; j += NT) sm.cstart[j] = 0;
     }
     for (int e = t; e < K; e += NT) {
-        const int j = (int)(cix[e] / DK);
+        const uint32_t p = cix[e];
+        const int j = (int)(p / DK), i = (int)(p - (uint32_t)j * DK);
+        kge[e] = sm.b.kf[i];
+        qge[e] = sm.b.qf[i];
         const int jp = e > 0 ? (int)(cix[e - 1] / DK) : -1;
         for (int jj = jp + 1; jj <= j; ++jj) sm.cstart[jj] = e;
         if (e == K - 1)
@@ -438,21 +469,36 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     __syncthreads();
 
     if (t < DV) {
+        // w and o of column j: the entries of the column in index order, then
+        // the stored deltas; the two chains are independent and interleaved
         const int j = t;
         const int lo = (int)sm.cstart[j], hi = (int)sm.cstart[j + 1];
-        float w = w0;
-        for (int e = lo; e < hi; ++e) w = fma_(cvl[e], sm.b.kf[cix[e] - j * DK], w);
+        float ck[kWMax], cq[kWMax];
 #pragma unroll
-        for (int m = 0; m < kWMax; ++m)
-            if (m < n) w = fma_(um[m], sm.ck[m], w);
+        for (int m = 0; m < kWMax; m += 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(&sm.ck[m]);
+            const float4 c = *reinterpret_cast<const float4 *>(&sm.cq[m]);
+            ck[m] = a.x; ck[m + 1] = a.y; ck[m + 2] = a.z; ck[m + 3] = a.w;
+            cq[m] = c.x; cq[m + 1] = c.y; cq[m + 2] = c.z; cq[m + 3] = c.w;
+        }
+        const float cqn = sm.cq[n];
+        float w = w0, o = o0;
+#pragma unroll 4
+        for (int e = lo; e < hi; ++e) {
+            const float v = cvl[e];
+            w = fma_(v, kge[e], w);
+            o = fma_(v, qge[e], o);
+        }
+#pragma unroll
+        for (int m = 0; m < kWMax; ++m) {
+            if (m < n) {
+                w = fma_(um[m], ck[m], w);
+                o = fma_(um[m], cq[m], o);
+            }
+        }
         const float u = beta * (vv - w);
         du[(size_t)n * DV + j] = u;
-        float o = o0;
-        for (int e = lo; e < hi; ++e) o = fma_(cvl[e], sm.b.qf[cix[e] - j * DK], o);
-#pragma unroll
-        for (int m = 0; m < kWMax; ++m)
-            if (m < n) o = fma_(um[m], sm.cq[m], o);
-        o = fma_(u, sm.cq[n], o);
+        o = fma_(u, cqn, o);
         A.o[unit * DV + j] = o;
     }
     if (t < DK) dkap[(size_t)n * DK + t] = sm.kr[t];
@@ -566,9 +612,11 @@ template <int DK, int DV, bool MIXED>
 __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     constexpr int CG = DV / 8;
     __shared__ LdsWin<DK, DV> sm;
-    extern __shared__ uint32_t win_entries[];  // [K] index, then [K] value
+    extern __shared__ uint32_t win_entries[];  // [K] index, value, gated key, gated query
     uint32_t *cix = win_entries;
     float *cvl = reinterpret_cast<float *>(win_entries + A.comps);
+    float *kge = cvl + A.comps;
+    float *qge = kge + A.comps;
     const size_t unit = blockIdx.x;
     const int b = (int)(unit / (size_t)A.H);
     const int h = (int)(unit - (size_t)b * A.H);
@@ -581,12 +629,12 @@ __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     switch (hd.width) {
-        case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
-        case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
-        case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
-        case 16: win_tile<DK, DV, 16>(A, hd, R, unit, sm, cix, cvl, t, rg, cg); break;
+        case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
+        case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
+        case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
+        case 16: win_tile<DK, DV, 16>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
         default:
-            if (MIXED) win_tile<DK, DV, 0>(A, hd, R, unit, sm, cix, cvl, t, rg, cg);
+            if (MIXED) win_tile<DK, DV, 0>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg);
             break;
     }
 }
@@ -741,7 +789,7 @@ hipError_t launch_grid(void (*k)(Args), const Args &a, hipStream_t s, size_t lds
     return hipErrorInvalidValue;
 
 hipError_t launch_step_win(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
-    const size_t entries = (size_t)a.comps * 8;  // index + value per compensation entry
+    const size_t entries = (size_t)a.comps * 16;  // index, value, gated key and query per entry
     const hipError_t e = [&]() -> hipError_t { STQ_WIN_DISPATCH(k_win, entries) }();
     if (e != hipSuccess) return e;
     STQ_WIN_DISPATCH(k_win_end, 0)
