@@ -228,11 +228,15 @@ struct Rows {
     uint32_t ro[8];  // byte offset of each row inside the head region
 };
 
+// W: the head's uniform row width, or 0 / kW4P for per-row widths.
+template <int W>
+constexpr bool per_row() { return W == 0 || W == kW4P; }
+
 template <int DV, int W>
 __device__ __forceinline__ void row_geometry(const Args &A, const HeadDesc &hd, int rg, Rows &rw) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        if (W) {
+        if (!per_row<W>()) {
             rw.w[r] = W;
             rw.ro[r] = (uint32_t)(8 * rg + r) * (uint32_t)(DV * W / 8);
         } else {
@@ -246,13 +250,13 @@ __device__ __forceinline__ void row_geometry(const Args &A, const HeadDesc &hd, 
 // Width of key row i of the head (uniform width or the row table).
 template <int W>
 __device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i) {
-    return W ? W : (int)row_width(A.rows[hd.rows + i]);
+    return !per_row<W>() ? W : (int)row_width(A.rows[hd.rows + i]);
 }
 
 // Whether the head has quantized rows: known from the width unless rows differ.
 template <int W>
 __device__ __forceinline__ bool has_quant(const HeadDesc &hd) {
-    return W == 16 ? false : (W != 0 ? true : hd.nquant > 0);
+    return W == 16 ? false : (!per_row<W>() ? true : hd.nquant > 0);
 }
 
 template <int N>

@@ -19,6 +19,7 @@
 struct stq_layout {
     stq_config cfg;                     // unit_bits cleared; widths live in `bits`
     bool mixed = false;                 // some head has rows of different widths
+    int step_mix = 0;                   // 0 none; 1 only 4-bit + pivot row heads; 2 other
     std::vector<uint8_t> bits;          // H or H*d_k unit widths
     std::vector<stq::HeadDesc> heads;   // [H]
     std::vector<uint32_t> rows;         // [H*d_k] row table
@@ -163,7 +164,16 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
         }
         d.width = (uint16_t)common;
         d.nquant = (uint16_t)nq;
-        if (common == 0) L->mixed = true;
+        if (common == 0) {
+            L->mixed = true;
+            bool w4p = true;
+            for (int i = 0; i < dk; ++i) {
+                const int b = keyrow ? L->bits[(size_t)h * dk + i] : L->bits[h];
+                w4p &= b == 4 || b == 16;
+            }
+            if (w4p) d.width = stq::kW4P;
+            L->step_mix = w4p ? (L->step_mix > 1 ? 2 : 1) : 2;
+        }
         d.cbytes = (uint32_t)p;
         p = up(p, 16);
         if (nq > 0) {
@@ -288,7 +298,7 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (L->cfg.window > 1)
         return launched(stq::launch_step_win(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "windowed decode step");
-    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "decode step");
+    return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->step_mix, s), "decode step");
 }
 
 stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids, float *d_state,

@@ -23,12 +23,17 @@ struct HeadDesc {
     uint32_t du;       // windowed: delta values [W][d_v] fp32
     uint32_t dkap;     // windowed: delta keys [W][d_k] fp32
     uint32_t rows;     // first entry of this head in the row table
-    uint16_t width;    // width shared by every row (4/6/8/16), 0 if rows differ
+    uint16_t width;    // width shared by every row (4/6/8/16); kW4P: 4-bit rows and
+                       // FP16 pivot rows; 0: rows of other differing widths
     uint16_t nquant;   // number of quantized (non-pivot) rows
     uint32_t cbytes;   // bytes of the code rows (a multiple of 16)
     uint32_t pad[3];
 };
 static_assert(sizeof(HeadDesc) == 64, "HeadDesc is 64 bytes");
+
+// HeadDesc::width of a head whose rows are 4-bit or FP16 pivots (and not all
+// the same): such heads are stepped by a path holding one dword per row.
+constexpr uint16_t kW4P = 20;
 
 // Row table entry: (byte offset of the row inside the head region) << 5 | width.
 __host__ __device__ inline uint32_t row_entry(uint32_t off, uint32_t width) { return (off << 5) | width; }
@@ -55,8 +60,9 @@ struct Args {
 };
 
 // Launchers (stq_kernels.hip).  Return the launch's hipError_t.  `mixed`: some
-// head of the layout has rows of different widths.
-hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s);
+// head of the layout has rows of different widths; `mix`: 0 none, 1 only
+// kW4P heads, 2 other mixed heads.
+hipError_t launch_step(const Args &a, int dk, int dv, int mix, hipStream_t s);
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s);
 // Windowed layouts (window > 1): stq_window.hip.

@@ -49,9 +49,22 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
     uint4 raw[8];
+    uint4 pv = make_uint4(0, 0, 0, 0);  // kW4P: the piece of the thread's first pivot row
+    int pr = -1;                        //      and that row
     if (PRE) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) raw[r] = make_uint4(p.raw[r], 0, 0, 0);
+    } else if (W == kW4P) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            raw[r] = make_uint4(0, 0, 0, 0);
+            if (rw.w[r] != 16) {
+                raw[r].x = *reinterpret_cast<const uint32_t *>(R + rw.ro[r] + 4 * cg);
+            } else if (pr < 0) {
+                pv = load_piece(R + rw.ro[r], cg, 16);
+                pr = r;
+            }
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
@@ -113,14 +126,16 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             const int w = rw.w[r];
             if (w == 16) {
                 const float a = sm.af[i];
-                const uint32_t hv[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
+                // kW4P: a second pivot row of the block is loaded here (rare)
+                const uint4 pc = W != kW4P ? raw[r] : r == pr ? pv : load_piece(R + rw.ro[r], cg, 16);
+                const uint32_t hv[4] = {pc.x, pc.y, pc.z, pc.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     x[r][2 * c] = a * f16v(hv[c]);
                     x[r][2 * c + 1] = a * f16v(hv[c] >> 16);
                 }
             } else {
-                dequant_row(raw[r], w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
+                dequant_row(raw[r], W == kW4P ? 4 : w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * cc[c];
             }
@@ -163,16 +178,19 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 // g / ngroups.  A group is one head, or two 4-bit heads: then the second
 // state's inputs are fetched before the first is computed, so their latency
 // is hidden behind that compute (workgroup barriers wait only for LDS
-// traffic).  MIXED: some head of the layout has rows of different widths
-// (KDA); without it the per-row width path is not compiled.
-template <int DK, int DV, bool MIXED>
+// traffic).  MIX: 0 if every head has one row width, 1 if the other heads
+// are all 4-bit rows with FP16 pivot rows (kW4P), 2 if some head mixes other
+// widths; only the per-row paths a layout needs are compiled, which saves
+// registers.
+template <int DK, int DV, int MIX>
 __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
     constexpr int CG = DV / 8;
     __shared__ Lds<DK, DV> sm;
-    const int ng = A.ngroups;
+    // ngroups == 0: every head alone (small batches keep more workgroups)
+    const int ng = A.ngroups ? A.ngroups : A.H;
     const int b = (int)(blockIdx.x / (uint32_t)ng);
     const int gi = (int)(blockIdx.x - (uint32_t)b * ng);
-    const uint32_t grp = A.groups[gi];
+    const uint32_t grp = A.ngroups ? A.groups[gi] : ((uint32_t)gi | 0xffff0000u);
     const int h1 = (int)(grp & 0xffffu), h2 = (int)(grp >> 16);
     const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
     const size_t u1 = (size_t)b * A.H + h1;
@@ -204,8 +222,11 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
         case 6: step_tile<DK, DV, 6, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 8: step_tile<DK, DV, 8, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 16: step_tile<DK, DV, 16, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case kW4P:
+            if (MIX >= 1) step_tile<DK, DV, kW4P, false>(A, hd1, R, u1, sm, t, rg, cg, none);
+            break;
         default:
-            if (MIXED) step_tile<DK, DV, 0, false>(A, hd1, R, u1, sm, t, rg, cg, none);
+            if (MIX == 2) step_tile<DK, DV, 0, false>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
     }
 }
@@ -336,18 +357,25 @@ hipError_t launch_dims(void (*k)(Args), const Args &a, hipStream_t s) {
     if (dk == 64 && dv == 128) return launch_dims<64, 128>(KERNEL<64, 128>, a, s);    \
     return hipErrorInvalidValue;
 
-template <int DK, int DV, bool MIXED>
-hipError_t launch_step_dims(const Args &a, hipStream_t s) {
+// Heads are paired only when the batch leaves enough workgroups to fill the
+// chip several times over.
+constexpr size_t kPairMinStates = 8192;
+
+template <int DK, int DV, int MIX>
+hipError_t launch_step_dims(Args a, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
-    void (*k)(Args) = k_step<DK, DV, MIXED>;
-    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * a.ngroups)), dim3(DK * DV / 64), 0, s, a);
+    if ((size_t)a.B * a.H < kPairMinStates) a.ngroups = 0;
+    const size_t per_request = a.ngroups ? (size_t)a.ngroups : (size_t)a.H;
+    void (*k)(Args) = k_step<DK, DV, MIX>;
+    hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * per_request)), dim3(DK * DV / 64), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_step(const Args &a, int dk, int dv, bool mixed, hipStream_t s) {
+hipError_t launch_step(const Args &a, int dk, int dv, int mix, hipStream_t s) {
 #define STQ_STEP(DK_, DV_)                                                                      \
     if (dk == DK_ && dv == DV_)                                                                 \
-        return mixed ? launch_step_dims<DK_, DV_, true>(a, s) : launch_step_dims<DK_, DV_, false>(a, s);
+        return mix == 2 ? launch_step_dims<DK_, DV_, 2>(a, s)                                  \
+                        : mix == 1 ? launch_step_dims<DK_, DV_, 1>(a, s) : launch_step_dims<DK_, DV_, 0>(a, s);
     STQ_STEP(128, 128)
     STQ_STEP(64, 64)
     STQ_STEP(128, 64)

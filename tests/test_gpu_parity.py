@@ -111,6 +111,19 @@ def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None)
         hs.close()
 
 
+def test_kda_4bit_rows_with_pivot_rows():
+    """KDA heads whose rows are 4-bit or FP16 pivots, with 8-row blocks holding
+    0, 1, 2 and 3 pivot rows (a thread owns one such block), a head without
+    pivot rows and an all-pivot head; d=128 and d=64."""
+    for d in (128, 64):
+        w = synth.WORKLOADS["kimi_kda"].with_(B=3, H=4, dk=d, dv=d, name=f"kda_4p_d{d}")
+        bits = np.full((w.H, d), 4, np.uint8)
+        bits[0, [0, 1, 9, 12, 13, 14, 40, d - 1]] = 16
+        bits[1, 5] = 16
+        bits[3, :] = 16
+        _run(w, 12, bits=bits.ravel(), check_slots_every=4, tag=f"kda-4p-d{d}")
+
+
 def test_qwen_gdn_all_units_all_steps():
     """B=64 x H=32, heads of 4/6/8 bits and an FP16 pivot head: every unit, all 256 steps."""
     _run(synth.WORKLOADS["qwen_gdn"], 256, check_slots_every=64, tag="qwen-all")
@@ -189,6 +202,34 @@ def test_invalid_slot_id_touches_nothing():
         assert np.array_equal(before[hs.slot_of[2]], after[hs.slot_of[2]])
         assert np.array_equal(before[np.setdiff1d(np.arange(4), hs.slot_of[[0, 1, 3]])],
                               after[np.setdiff1d(np.arange(4), hs.slot_of[[0, 1, 3]])])
+    finally:
+        hs.close()
+
+
+def test_invalid_slot_id_in_paired_heads():
+    """A batch large enough for paired 4-bit heads (256 x 32 states): an
+    invalid slot id gives NaN outputs for every head of that request (paired
+    or not) and leaves the pool unchanged; the other requests match the
+    oracle."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["serving_gdn"].with_(B=256)
+    follow = [(b, h) for b in (0, 7, 255) for h in range(w.H)]
+    hs = _harness(w, follow=follow)
+    try:
+        hs.load_full(0)
+        o_gpu, o_ref = hs.step(hs.load_followed(0), idx_in_x=True)
+        _check_step(o_gpu, o_ref, hs.follow, 0, "paired-invalid")
+        before = hs.slot_bytes_gpu()
+        ids = hs.slot_ids.clone()
+        ids[7] = -3
+        stq.decode_step(hs.pool, ids, hs.q, hs.k, hs.v, hs.a, hs.beta, hs.o)
+        torch.cuda.synchronize()
+        o = hs.o.cpu().numpy()
+        assert np.isnan(o[7]).all()
+        assert np.isfinite(o[[0, 255]]).all()
+        after = hs.slot_bytes_gpu()
+        assert np.array_equal(before[hs.slot_of[7]], after[hs.slot_of[7]])
     finally:
         hs.close()
 
