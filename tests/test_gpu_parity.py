@@ -146,6 +146,14 @@ def test_serving_gdn_sampled_units_all_2048_steps():
     assert np.isfinite(e).all()
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64)])
+def test_paired_heads_other_head_sizes(dk, dv):
+    """4-bit GDN heads in pairs (batch of 256 x 32 states) at the other head
+    sizes: 64 followed units over 12 steps, slot bytes compared at the end."""
+    w = synth.WORKLOADS["serving_gdn"].with_(B=256, dk=dk, dv=dv, name=f"serving_{dk}x{dv}")
+    _run_sampled(w, 12, 64, seed=20 + dk + dv, tag=f"pairs-{dk}x{dv}")
+
+
 def test_kimi_kda_all_units_32_steps():
     """B=256 x H=32 KDA (4-bit rows + 41 FP16 pivot rows), outlier start: every unit, 32 steps."""
     _run(synth.WORKLOADS["kimi_kda"], 32, check_slots_every=16, tag="kimi-all")
