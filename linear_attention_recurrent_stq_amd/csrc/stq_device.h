@@ -312,17 +312,22 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         }
     }
     if (cs || emit_o) __syncthreads();
-    if (t < DV) {
-        if (emit_o) A.o[unit * DV + t] = col_sum<DK, DV>(sm, t);
+    // o of column t, and the new scale of column tc: with at least 2 d_v
+    // threads, threads [0, d_v) combine o while threads [d_v, 2 d_v) form the
+    // scales, so the two serial combines run side by side
+    constexpr int NT = DK * DV / 64;
+    if (emit_o && t < DV) A.o[unit * DV + t] = col_sum<DK, DV>(sm, t);
+    const int tc = (emit_o && NT >= 2 * DV) ? t - DV : t;
+    if (tc >= 0 && tc < DV) {
         float ic = 1.0f;
         if (cs) {
-            const float C = col_max<DK, DV>(sm, t);
+            const float C = col_max<DK, DV>(sm, tc);
             const uint32_t hc = h16(C);
             const float cv = f16v(hc);
             ic = cv > 0.0f ? 1.0f / cv : 0.0f;
-            reinterpret_cast<uint16_t *>(R + hd.cs)[t] = (uint16_t)hc;
+            reinterpret_cast<uint16_t *>(R + hd.cs)[tc] = (uint16_t)hc;
         }
-        sm.ic[t] = ic;
+        sm.ic[tc] = ic;
     }
     if (!quant) {
         // all rows are FP16 pivots: store and finish
