@@ -406,6 +406,49 @@ def test_quantized_step_tracks_fp64(ora, width, tol):
             assert np.max(np.abs(o - o64)) <= tol * np.max(np.abs(o64))
 
 
+@pytest.mark.parametrize("width", [4, 6, 8])
+@pytest.mark.parametrize("kda", [False, True])
+def test_quantized_step_injects_at_most_half_a_step(ora, width, kda):
+    """Each quantized step is the exact (fp64) gated delta-rule step of the
+    previously stored state plus a quantization injection of at most half a
+    step r'_i c'_j per entry (half an fp16 ulp on pivot rows), and o is the
+    exact output of the updated state before requantization, to fp32
+    rounding.  Element by element this pins the update (sign, orientation,
+    gate placement), the dequantization scales, that o uses the updated state,
+    and rounding to nearest."""
+    rng = np.random.default_rng(40 + width + 7 * kda)
+    dk = dv = 32
+    if kda:
+        bits = np.full(dk, width, np.uint8)
+        bits[[3, 20]] = 16
+        cfg = _cfg(ora, dk=dk, dv=dv, keyrow=True, gate_vec=True, bits=bits)
+    else:
+        bits = np.full(dk, width, np.uint8)
+        cfg = _cfg(ora, dk=dk, dv=dv, width=width)
+    piv = bits == 16
+    lay = cfg.head_layout(0)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, (rng.standard_normal((dk, dv)) * 0.5).astype(np.float32))
+    for t in range(24):
+        prev = cfg.unpack_head(slot, 0).astype(np.float64)
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0.85, 1.0, dk if kda else 1)
+        b = rng.uniform(0.3, 1.0)
+        k, q, v, a = (x.astype(np.float32) for x in (k, q, v, a))
+        o = cfg.step_head(slot, 0, q, k, v, a, b)
+        exact = prev.copy()
+        o64 = ora.step_f64(exact, q, k, v, a, float(np.float32(b)), kda)
+        assert np.max(np.abs(o - o64)) <= 1e-5 * np.max(np.abs(o64)) + 1e-7, t
+        new = cfg.unpack_head(slot, 0).astype(np.float64)
+        _, _, r, c = slotcodec.read_head(slot, lay, bits, dk, dv, True, True)
+        half = 0.5 * np.outer(r.astype(np.float64), c.astype(np.float64))
+        bound = np.where(piv[:, None], 2.0 ** -11 * np.abs(exact), half * (1 + 1e-5)) \
+            + 1e-6 * np.abs(exact) + 1e-30
+        assert np.all(np.abs(new - exact) <= bound), t
+
+
 def test_all_pivot_is_fp16_recurrence(ora):
     """All units FP16 pivots: the state after each step is the fp16 rounding of
     the fp32 step applied to the previous fp16 state (numpy half casts)."""
