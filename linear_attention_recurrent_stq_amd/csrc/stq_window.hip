@@ -35,8 +35,8 @@ template <int DK, int DV>
 struct LdsW {
     Lds<DK, DV> b;            // per-step arrays (partials, row/column constants, 1/c', 1/r')
     float gn[DK];             // cumulative gate
-    float kst[kWMax][DK];     // decayed delta keys
-    float ust[kWMax][DV];     // delta values
+    alignas(16) float kst[kWMax][DK];  // decayed delta keys
+    alignas(16) float ust[kWMax][DV];  // delta values
     uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
     float cvl[kKMax];         // compensation value
     uint32_t ckey[kCandMax];  // candidate keys
@@ -524,8 +524,29 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
     const float *du = reinterpret_cast<const float *>(R + hd.du);
     const float *dkap = reinterpret_cast<const float *>(R + hd.dkap);
     base_constants<DK, DV, W>(A, hd, R, sm.b, t);
-    for (int e = t; e < n * DK; e += NT) sm.kst[e / DK][e % DK] = dkap[e];
-    for (int e = t; e < n * DV; e += NT) sm.ust[e / DV][e % DV] = du[e];
+    {
+        // stage the W deltas in LDS: every 16-byte load is issued before the
+        // first LDS write, so the staging costs one memory round trip
+        constexpr int PER = (kWMax * (DK > DV ? DK : DV) / 4 + NT - 1) / NT;
+        const int nk = n * DK / 4, nu = n * DV / 4;
+        const float4 *ks = reinterpret_cast<const float4 *>(dkap);
+        const float4 *us = reinterpret_cast<const float4 *>(du);
+        float4 kv[PER], uv[PER];
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = t + p * NT;
+            kv[p] = ks[e < nk ? e : 0];  // index 0 is always valid (n >= 1)
+            uv[p] = us[e < nu ? e : 0];
+        }
+        float4 *kd = reinterpret_cast<float4 *>(&sm.kst[0][0]);
+        float4 *ud = reinterpret_cast<float4 *>(&sm.ust[0][0]);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = t + p * NT;
+            if (e < nk) kd[e] = kv[p];
+            if (e < nu) ud[e] = uv[p];
+        }
+    }
     if (t < DK) sm.gn[t] = gmem[t];
     for (int e = t; e < K; e += NT) {
         sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
