@@ -17,7 +17,8 @@
  *    one scalar per head (GDN).
  *  - Quantized storage in the STEPQuant style (essay, temporal-axis and
  *    spatial-axis paragraphs): a bit width per unit (a whole head for GDN, one
- *    key row for KDA) from {4,6,8}, FP16 pivot units (width 16), and a row
+ *    key row for KDA) from {4,6,8}, FP16 pivot units (width 16), fp32 units
+ *    (width 32: the unquantized state the pages compare against), and a row
  *    scale and a column scale per state (dual-axis fitting), refitted at every
  *    step from absolute maxima (essay, experiment-design paragraph: the
  *    dual-axis scales are recomputed each decode step).
@@ -43,7 +44,7 @@
  * Per-step mode (window == 1), one state:
  *   decay+dequant  g_i = RN(a_i*r_i);  A_ij = RN(RN(n_ij*g_i)*c_j)
  *                  (no column scale: A_ij = RN(n_ij*g_i));
- *                  pivot row: A_ij = RN(a_i*h_ij)
+ *                  pivot row: A_ij = RN(a_i*h_ij); fp32 row: A_ij = RN(a_i*m_ij)
  *   read           w_j = csum(A_.j, k)
  *   delta          u_j = RN(beta*RN(v_j - w_j))
  *   write          M_ij = fma(k_i, u_j, A_ij)
@@ -57,7 +58,8 @@
  *                  |Z_ij*ir_i| < qmax + 1/2, so the clamp below only acts when
  *                  the step saturated at 65504.
  *   codes          n'_ij = clamp(rne(Z_ij*ir_i exactly), -qmax_i, qmax_i)
- *                  pivot row: h'_ij = H(M_ij)
+ *                  pivot row: h'_ij = H(M_ij); fp32 row: m'_ij = M_ij
+ *                  (pivot and fp32 rows are left out of both scale maxima)
  *
  * Windowed mode (window W > 1), base B_ij = RN(n_ij*r_i*c_j) (pivot: h_ij;
  * compensation positions: their fp32 value), cumulative gate g (1 at a
@@ -93,7 +95,8 @@ typedef struct {
     int32_t cscale_f16;     /* 1: fp16 column scales, 0: none */
     int32_t window;         /* 1: requantize every step; W > 1: windowed */
     int32_t comps;          /* K fp32 compensation entries (windowed only) */
-    const uint8_t *bits;    /* H (per head) or H*dk (per key row) widths, 16 = pivot */
+    const uint8_t *bits;    /* H (per head) or H*dk (per key row) widths, 16 = pivot,
+                               32 = fp32 (every-step mode only) */
 } ora_cfg;
 
 /* Byte offsets of one head region inside a slot. */
@@ -103,7 +106,7 @@ typedef struct {
     size_t rs, cs;          /* row scales, column scales (0 if absent) */
     size_t wn, g, cidx, cval, du, dkap;  /* windowed: count, gate, comps, deltas */
     size_t bytes;           /* region size */
-    int32_t nquant;         /* number of non-pivot rows */
+    int32_t nquant;         /* number of quantized (4/6/8-bit) rows */
 } ora_head;
 
 static int row_bits(const ora_cfg *c, int h, int i) {
@@ -130,7 +133,7 @@ static size_t head_layout(const ora_cfg *c, int h, size_t base, ora_head *o) {
     for (int i = 0; i < c->dk; ++i) {
         int b = row_bits(c, h, i);
         p += (size_t)c->dv * b / 8;
-        if (b != 16) ++nq;
+        if (b < 16) ++nq;
     }
     o->nquant = nq;
     p = up(p, 16);
@@ -276,6 +279,7 @@ static int qmax_of(int b) { return (1 << (b - 1)) - 1; }
 typedef struct {
     int32_t *n;      /* dk*dv */
     uint16_t *hv;    /* dk*dv, pivot rows */
+    float *fv;       /* dk*dv, fp32 rows */
     int *bw;         /* dk widths */
     float *r, *c;    /* dk, dv */
     float *g;        /* dk (windowed) */
@@ -289,6 +293,7 @@ static void unit_alloc(const ora_cfg *c, ora_unit *u) {
     size_t e = (size_t)c->dk * c->dv;
     u->n = calloc(e, sizeof(int32_t));
     u->hv = calloc(e, sizeof(uint16_t));
+    u->fv = calloc(e, sizeof(float));
     u->bw = calloc((size_t)c->dk, sizeof(int));
     u->r = calloc((size_t)c->dk, sizeof(float));
     u->c = calloc((size_t)c->dv, sizeof(float));
@@ -301,7 +306,7 @@ static void unit_alloc(const ora_cfg *c, ora_unit *u) {
 }
 
 static void unit_free(ora_unit *u) {
-    free(u->n); free(u->hv); free(u->bw); free(u->r); free(u->c); free(u->g);
+    free(u->n); free(u->hv); free(u->fv); free(u->bw); free(u->r); free(u->c); free(u->g);
     free(u->cidx); free(u->cval); free(u->du); free(u->dkap);
 }
 
@@ -315,8 +320,10 @@ static void unit_read(const ora_cfg *c, int h, const uint8_t *slot, ora_unit *u)
         u->bw[i] = b;
         for (int j = 0; j < c->dv; ++j) {
             uint32_t raw = get_bits(R + rowoff, (size_t)j * b, b);
-            if (b == 16) { u->hv[(size_t)i * c->dv + j] = (uint16_t)raw; u->n[(size_t)i * c->dv + j] = 0; }
-            else u->n[(size_t)i * c->dv + j] = (int32_t)raw - (1 << (b - 1));
+            size_t e = (size_t)i * c->dv + j;
+            if (b == 32) { memcpy(&u->fv[e], &raw, 4); u->n[e] = 0; }
+            else if (b == 16) { u->hv[e] = (uint16_t)raw; u->n[e] = 0; }
+            else u->n[e] = (int32_t)raw - (1 << (b - 1));
         }
         rowoff += (size_t)c->dv * b / 8;
     }
@@ -347,8 +354,11 @@ static void unit_write(const ora_cfg *c, int h, uint8_t *slot, const ora_unit *u
     for (int i = 0; i < c->dk; ++i) {
         int b = row_bits(c, h, i);
         for (int j = 0; j < c->dv; ++j) {
-            uint32_t raw = (b == 16) ? u->hv[(size_t)i * c->dv + j]
-                                     : (uint32_t)(u->n[(size_t)i * c->dv + j] + (1 << (b - 1)));
+            size_t e = (size_t)i * c->dv + j;
+            uint32_t raw;
+            if (b == 32) memcpy(&raw, &u->fv[e], 4);
+            else if (b == 16) raw = u->hv[e];
+            else raw = (uint32_t)(u->n[e] + (1 << (b - 1)));
             put_bits(R + rowoff, (size_t)j * b, b, raw);
         }
         rowoff += (size_t)c->dv * b / 8;
@@ -379,7 +389,8 @@ static void dequant_base(const ora_cfg *c, const ora_unit *u, float *B, int with
     for (int i = 0; i < c->dk; ++i)
         for (int j = 0; j < c->dv; ++j) {
             size_t e = (size_t)i * c->dv + j;
-            if (u->bw[i] == 16) B[e] = f16_val(u->hv[e]);
+            if (u->bw[i] == 32) B[e] = u->fv[e];
+            else if (u->bw[i] == 16) B[e] = f16_val(u->hv[e]);
             else B[e] = ((float)u->n[e] * u->r[i]) * u->c[j];
         }
     if (c->window > 1 && with_comps)
@@ -399,7 +410,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
         float C = 0.0f;
         for (int i = 0; i < dk; ++i) {
             size_t e = (size_t)i * dv + j;
-            if (u->bw[i] == 16 || (skip && skip[e])) continue;
+            if (u->bw[i] >= 16 || (skip && skip[e])) continue;
             float a = fabsf(M[e]);
             if (a > C) C = a;
         }
@@ -407,11 +418,13 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
         ic[j] = u->c[j] > 0.0f ? 1.0f / u->c[j] : 0.0f;
     }
     for (int i = 0; i < dk; ++i) {
-        if (u->bw[i] == 16) {
+        if (u->bw[i] >= 16) {
+            /* pivot rows keep the fp16 of the state, fp32 rows the state itself */
             u->r[i] = 0.0f;
             for (int j = 0; j < dv; ++j) {
                 size_t e = (size_t)i * dv + j;
-                u->hv[e] = H(M[e]);
+                if (u->bw[i] == 32) u->fv[e] = M[e];
+                else u->hv[e] = H(M[e]);
                 u->n[e] = 0;
             }
             continue;
@@ -459,7 +472,7 @@ static void select_comps(const ora_cfg *c, ora_unit *u, const float *M, uint8_t 
     size_t e = (size_t)c->dk * c->dv, m = 0;
     ora_ent *all = malloc(sizeof(ora_ent) * e);
     for (int i = 0; i < c->dk; ++i) {
-        if (u->bw[i] == 16) continue;
+        if (u->bw[i] >= 16) continue;
         for (int j = 0; j < c->dv; ++j) {
             all[m].mag = fabsf(M[(size_t)i * c->dv + j]);
             all[m].idx = (uint32_t)((size_t)j * c->dk + i);
@@ -550,7 +563,8 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
             float gi = ai[i] * u.r[i];
             for (int j = 0; j < dv; ++j) {
                 size_t x = (size_t)i * dv + j;
-                if (u.bw[i] == 16) A[x] = ai[i] * f16_val(u.hv[x]);
+                if (u.bw[i] == 32) A[x] = ai[i] * u.fv[x];
+                else if (u.bw[i] == 16) A[x] = ai[i] * f16_val(u.hv[x]);
                 else if (c->cscale_f16) A[x] = ((float)u.n[x] * gi) * u.c[j];
                 else A[x] = (float)u.n[x] * gi;
             }

@@ -449,6 +449,38 @@ def test_quantized_step_injects_at_most_half_a_step(ora, width, kda):
         assert np.all(np.abs(new - exact) <= bound), t
 
 
+def test_fp32_units_are_the_fp32_recurrence(ora):
+    """Heads of fp32 units (width 32) step exactly like the unquantized fp32
+    step (itself pinned by the closed forms above), bit for bit, next to a
+    quantized head and a pivot head that do not affect them; pack and unpack
+    of an fp32 head are the identity."""
+    rng = np.random.default_rng(77)
+    dk = dv = 16
+    for gate_vec in (False, True):
+        bits = np.array([32, 4, 16, 32], np.uint8)
+        cfg = _cfg(ora, H=4, dk=dk, dv=dv, gate_vec=gate_vec, bits=bits)
+        lay = cfg.head_layout(0)
+        assert lay["nquant"] == 0 and lay["bytes"] == (dk * dv * 4 + 255) // 256 * 256
+        slot = cfg.new_slot()
+        M0 = (rng.standard_normal((dk, dv)) * 0.3).astype(np.float32)
+        cfg.pack_head(slot, 0, M0)
+        cfg.pack_head(slot, 3, M0)
+        assert np.array_equal(cfg.unpack_head(slot, 0), M0)
+        M = M0.copy()
+        for t in range(12):
+            k = rng.standard_normal(dk).astype(np.float32)
+            q = rng.standard_normal(dk).astype(np.float32)
+            v = rng.standard_normal(dv).astype(np.float32)
+            a = rng.uniform(0.8, 1.0, dk if gate_vec else 1).astype(np.float32)
+            b = np.float32(rng.uniform(0.2, 1.0))
+            want = ora.step_f32(M, q, k, v, a, b, gate_vec)
+            for h in range(4):
+                o = cfg.step_head(slot, h, q, k, v, a, b)
+                if bits[h] == 32:
+                    assert np.array_equal(o, want), (t, h)
+                    assert np.array_equal(cfg.unpack_head(slot, h), M), (t, h)
+
+
 def test_all_pivot_is_fp16_recurrence(ora):
     """All units FP16 pivots: the state after each step is the fp16 rounding of
     the fp32 step applied to the previous fp16 state (numpy half casts)."""
