@@ -41,7 +41,7 @@ def state_bytes(w: synth.Workload, bits: np.ndarray) -> list[int]:
     for h in range(w.H):
         wid = bits[h * w.dk:(h + 1) * w.dk] if w.unit == "keyrow" else np.full(w.dk, bits[h])
         codes = int(sum(w.dv * int(b) // 8 for b in wid))
-        nq = int((wid != 16).sum())
+        nq = int((wid < 16).sum())  # quantized rows (not fp16 pivots or fp32 rows)
         scales = (w.dk * (2 if w.row_scale == "f16" else 4) + (2 * w.dv if w.col_scale == "f16" else 0)) if nq else 0
         out.append(codes + scales)
     return out

@@ -63,7 +63,8 @@ typedef struct {
     int32_t window;          /* 1: requantize every step; 2..16: windowed */
     int32_t comps;           /* windowed: K fp32 compensation entries, 0..1024 */
     const uint8_t *unit_bits;/* host; H (per head) or H*d_k (per key row) widths
-                                in {4,6,8,16}; 16 = FP16 pivot unit */
+                                in {4,6,8,16,32}; 16 = FP16 pivot unit; 32 = fp32
+                                (unquantized) unit: window 1 only, whole heads */
 } stq_config;
 
 typedef struct stq_layout stq_layout;   /* opaque, host-owned by the library */
@@ -79,8 +80,9 @@ const char *stq_last_error(void);
  * experiment-design paragraph: widths and pivots are fixed offline, scales are
  * refitted online).  On success *out owns a new layout; free it with
  * stq_layout_free.  Errors: STQ_ERR_INVALID (NULL, H < 1, widths not in
- * {4,6,8,16}, bad enums, comps without window, comps > non-pivot entries),
- * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 16).
+ * {4,6,8,16,32}, bad enums, comps without window, comps > quantized entries),
+ * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 16, fp32 units in the
+ * windowed mode or on part of a head's key rows).
  */
 stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out);
 

@@ -228,7 +228,8 @@ struct Rows {
     uint32_t ro[8];  // byte offset of each row inside the head region
 };
 
-// W: the head's uniform row width, or 0 / kW4P for per-row widths.
+// W: the head's uniform row width (32: fp32 rows), or 0 / kW4P for per-row
+// widths.
 template <int W>
 constexpr bool per_row() { return W == 0 || W == kW4P; }
 
@@ -256,7 +257,7 @@ __device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i
 // Whether the head has quantized rows: known from the width unless rows differ.
 template <int W>
 __device__ __forceinline__ bool has_quant(const HeadDesc &hd) {
-    return W == 16 ? false : (!per_row<W>() ? true : hd.nquant > 0);
+    return (W == 16 || W == 32) ? false : (!per_row<W>() ? true : hd.nquant > 0);
 }
 
 template <int N>
@@ -330,9 +331,17 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         sm.ic[tc] = ic;
     }
     if (!quant) {
-        // all rows are FP16 pivots: store and finish
+        // all rows are FP16 pivots (or fp32 rows, stored as they are): store and finish
 #pragma unroll
-        for (int r = 0; r < 8; ++r) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
+        for (int r = 0; r < 8; ++r) {
+            if (W == 32) {
+                float4 *p = reinterpret_cast<float4 *>(R + rw.ro[r] + 32 * cg);
+                p[0] = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
+                p[1] = make_float4(x[r][4], x[r][5], x[r][6], x[r][7]);
+            } else {
+                store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
+            }
+        }
         return;
     }
     __syncthreads();

@@ -65,10 +65,21 @@ stq_status check_cfg(const stq_config *c) {
     const size_t n = (size_t)c->H * (c->unit == STQ_UNIT_KEYROW ? c->d_k : 1);
     for (size_t i = 0; i < n; ++i) {
         const uint8_t b = c->unit_bits[i];
-        if (b != 4 && b != 6 && b != 8 && b != 16) {
+        if (b != 4 && b != 6 && b != 8 && b != 16 && b != 32) {
             char m[96];
-            std::snprintf(m, sizeof m, "unit_bits[%zu] = %u is not in {4,6,8,16}", i, (unsigned)b);
+            std::snprintf(m, sizeof m, "unit_bits[%zu] = %u is not in {4,6,8,16,32}", i, (unsigned)b);
             return fail(STQ_ERR_INVALID, m);
+        }
+        if (b == 32 && c->window > 1)
+            return fail(STQ_ERR_UNSUPPORTED, "fp32 units (width 32) need the every-step mode (window 1)");
+    }
+    if (c->unit == STQ_UNIT_KEYROW) {
+        // an fp32 unit is a whole head: its key rows are all fp32 or none is
+        for (int h = 0; h < c->H; ++h) {
+            int n32 = 0;
+            for (int i = 0; i < c->d_k; ++i) n32 += c->unit_bits[(size_t)h * c->d_k + i] == 32;
+            if (n32 != 0 && n32 != c->d_k)
+                return fail(STQ_ERR_UNSUPPORTED, "fp32 units (width 32) must cover whole heads");
         }
     }
     return STQ_OK;
@@ -159,7 +170,7 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
             const int b = keyrow ? L->bits[(size_t)h * dk + i] : L->bits[h];
             L->rows[(size_t)h * dk + i] = stq::row_entry((uint32_t)p, (uint32_t)b);
             p += (size_t)dv * b / 8;
-            nq += b != 16;
+            nq += b < 16;
             common = (common == -1 || common == b) ? b : 0;
         }
         d.width = (uint16_t)common;

@@ -51,7 +51,17 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     uint4 raw[8];
     uint4 pv = make_uint4(0, 0, 0, 0);  // kW4P: the piece of the thread's first pivot row
     int pr = -1;                        //      and that row
-    if (PRE) {
+    float x[8][8];                      // the thread's 8 x 8 block of the state
+    if (W == 32) {
+        // fp32 rows: the 8 values of each row piece straight into the block
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float4 *p = reinterpret_cast<const float4 *>(R + rw.ro[r] + 32 * cg);
+            const float4 a0 = p[0], a1 = p[1];
+            x[r][0] = a0.x; x[r][1] = a0.y; x[r][2] = a0.z; x[r][3] = a0.w;
+            x[r][4] = a1.x; x[r][5] = a1.y; x[r][6] = a1.z; x[r][7] = a1.w;
+        }
+    } else if (PRE) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) raw[r] = make_uint4(p.raw[r], 0, 0, 0);
     } else if (W == kW4P) {
@@ -100,7 +110,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             const float g = a * ri;
             sm.g[i] = g;
             sm.g16[i] = g * 0.0625f;
-            sm.nog[i] = w != 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
+            sm.nog[i] = w < 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
             sm.af[i] = a;
             sm.kf[i] = load1(A.k, A.io_bf16, unit * DK + i);
             sm.qf[i] = load1(A.q, A.io_bf16, unit * DK + i);
@@ -115,7 +125,6 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     // partial sums over the thread's 8 rows accumulated as the rows come in.
     // Vectors are read from LDS where they are used, so that none of them is
     // held across a barrier.
-    float x[8][8];
     {
         float kk[8], cc[8], s[8];
         lds_read8(&sm.kf[8 * rg], kk, 0);
@@ -124,7 +133,11 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         for (int r = 0; r < 8; ++r) {
             const int i = 8 * rg + r;
             const int w = rw.w[r];
-            if (w == 16) {
+            if (W == 32) {
+                const float a = sm.af[i];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) x[r][c] = a * x[r][c];
+            } else if (w == 16) {
                 const float a = sm.af[i];
                 // kW4P: a second pivot row of the block is loaded here (rare)
                 const uint4 pc = W != kW4P ? raw[r] : r == pr ? pv : load_piece(R + rw.ro[r], cg, 16);
@@ -222,6 +235,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
         case 6: step_tile<DK, DV, 6, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 8: step_tile<DK, DV, 8, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 16: step_tile<DK, DV, 16, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 32: step_tile<DK, DV, 32, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case kW4P:
             if (MIX >= 1) step_tile<DK, DV, kW4P, false>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
@@ -267,6 +281,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_pack(Args A) {
         case 6: pack_tile<DK, DV, 6>(A, hd, R, sm, t, rg, cg, unit); break;
         case 8: pack_tile<DK, DV, 8>(A, hd, R, sm, t, rg, cg, unit); break;
         case 16: pack_tile<DK, DV, 16>(A, hd, R, sm, t, rg, cg, unit); break;
+        case 32: pack_tile<DK, DV, 32>(A, hd, R, sm, t, rg, cg, unit); break;
         default: pack_tile<DK, DV, 0>(A, hd, R, sm, t, rg, cg, unit); break;
     }
 }
@@ -296,13 +311,19 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack(Args A) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int i = 8 * rg + r;
-        const uint4 raw = load_piece(R + rw.ro[r], cg, rw.w[r]);
         float x[8];
-        if (rw.w[r] == 16) {
+        if (rw.w[r] == 32) {
+            const float4 *p = reinterpret_cast<const float4 *>(R + rw.ro[r] + 32 * cg);
+            const float4 a0 = p[0], a1 = p[1];
+            x[0] = a0.x; x[1] = a0.y; x[2] = a0.z; x[3] = a0.w;
+            x[4] = a1.x; x[5] = a1.y; x[6] = a1.z; x[7] = a1.w;
+        } else if (rw.w[r] == 16) {
+            const uint4 raw = load_piece(R + rw.ro[r], cg, 16);
             const uint32_t hv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) { x[2 * c] = f16v(hv[c]); x[2 * c + 1] = f16v(hv[c] >> 16); }
         } else {
+            const uint4 raw = load_piece(R + rw.ro[r], cg, rw.w[r]);
             const float ri = !quant ? 0.0f
                              : A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
                                       : reinterpret_cast<const float *>(R + hd.rs)[i];

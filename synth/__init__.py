@@ -127,6 +127,11 @@ WORKLOADS = {
         "serving_gdn", 4, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
         row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.02,
         init="zero", layers=4, desc="GDN pool B=512 H=32 d=128 L=4, avg 4 bit, 2% fp16 pivot heads"),
+    "serving_fp32": Workload(
+        "serving_fp32", 6, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
+        row_scale="f16", col_scale="f16", io="bf16", bits="fp32", pivot_frac=0.0,
+        init="zero", layers=4,
+        desc="the serving shape with fp32 (unquantized) state: the comparison point"),
     "windowed_kda": Workload(
         "windowed_kda", 5, B=512, H=32, dk=128, dv=128, T=1024, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,
@@ -143,9 +148,9 @@ def _perm(key, n: int) -> np.ndarray:
 
 
 def unit_bits(w: Workload, layer: int = 0) -> np.ndarray:
-    """Per-unit widths in {4,6,8,16}: one per head (GDN) or per (head, key row) (KDA).
+    """Per-unit widths in {4,6,8,16,32}: one per head (GDN) or per (head, key row) (KDA).
 
-    16 marks an FP16 pivot unit.  The pivot count is max(1, round(frac * units))
+    16 marks an FP16 pivot unit, 32 an fp32 (unquantized) unit.  The pivot count is max(1, round(frac * units))
     when frac > 0.  Non-pivot widths follow the maximum-entropy split over
     {4,6,8} with the stated mean: mean 6 gives equal thirds (remainder to 6),
     mean 4 can only be met by all-4.
@@ -161,6 +166,8 @@ def unit_bits(w: Workload, layer: int = 0) -> np.ndarray:
         bits[rest] = 6
     elif w.bits in ("uniform8",):
         bits[rest] = 8
+    elif w.bits == "fp32":
+        bits[rest] = 32
     elif w.bits == "avg4":
         bits[rest] = 4
     elif w.bits == "avg6":

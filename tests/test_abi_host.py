@@ -101,6 +101,27 @@ def test_config_rejected(stq, field, value, status):
     assert stq.library().stq_last_error().decode()
 
 
+def test_fp32_units(stq, ora):
+    """Width 32 (fp32, unquantized units) is a whole-head width of the
+    every-step mode: accepted there, with the oracle's layout; rejected in the
+    windowed mode and on part of a KDA head's key rows."""
+    bits = np.array([32, 4, 16, 32], np.uint8)
+    L = stq.Layout(4, 128, 128, bits)
+    o = ora.Cfg(4, 128, 128, False, False, True, True, 1, 0, bits)
+    assert L.slot_bytes == o.slot_bytes
+    assert L.head(0) == (0, 128 * 128 * 4)
+    kda = np.full(2 * 64, 4, np.uint8)
+    kda[:64] = 32                          # head 0 all fp32, head 1 4-bit
+    stq.Layout(2, 64, 64, kda, unit=stq.UNIT_KEYROW, gate=stq.GATE_KEYVEC)
+    kda[64] = 32                           # one fp32 row in head 1
+    with pytest.raises(stq.StqError) as e:
+        stq.Layout(2, 64, 64, kda, unit=stq.UNIT_KEYROW, gate=stq.GATE_KEYVEC)
+    assert "whole heads" in str(e.value)
+    with pytest.raises(stq.StqError) as e:
+        stq.Layout(4, 128, 128, bits, window=4, comps=8)
+    assert "window" in str(e.value)
+
+
 def test_bad_widths_and_too_many_comps(stq):
     with pytest.raises(stq.StqError) as e:
         stq.Layout(2, 64, 64, np.array([4, 5], np.uint8))

@@ -124,6 +124,16 @@ def test_kda_4bit_rows_with_pivot_rows():
         _run(w, 12, bits=bits.ravel(), check_slots_every=4, tag=f"kda-4p-d{d}")
 
 
+def test_fp32_heads():
+    """fp32 (unquantized) heads: the serving shape with every head fp32, and a
+    layout mixing fp32, 4/6/8-bit and FP16 pivot heads; all units, slot bytes
+    compared every few steps."""
+    _run(synth.WORKLOADS["serving_fp32"].with_(B=16), 8, check_slots_every=4, tag="fp32")
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=6, H=6, name="qwen_mixed_fp32")
+    bits = np.array([32, 4, 16, 6, 32, 8], np.uint8)
+    _run(w, 10, bits=bits, check_slots_every=5, tag="fp32-mixed")
+
+
 def test_qwen_gdn_all_units_all_steps():
     """B=64 x H=32, heads of 4/6/8 bits and an FP16 pivot head: every unit, all 256 steps."""
     _run(synth.WORKLOADS["qwen_gdn"], 256, check_slots_every=64, tag="qwen-all")
