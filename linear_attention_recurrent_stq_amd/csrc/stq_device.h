@@ -74,9 +74,15 @@ __device__ __forceinline__ uint4 load_piece(const uint8_t *row, int cg, int w) {
         const uint2 v = *reinterpret_cast<const uint2 *>(row + 8 * cg);
         r.x = v.x; r.y = v.y;
     } else if (w == 6) {
-        const uint16_t *p = reinterpret_cast<const uint16_t *>(row + 6 * cg);
-        r.x = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
-        r.y = p[2];
+        // 6 bytes at a 2-byte aligned offset: the two dwords around them,
+        // shifted (they stay inside the row: 6*cg + 6 <= row bytes, and the
+        // aligned start is at most 2 bytes before the piece)
+        const uint32_t off = 6u * (uint32_t)cg;
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(row + (off & ~3u));
+        const uint32_t lo = q[0], hi = q[1];
+        const uint32_t sh = (off & 3u) * 8u;  // 0 or 16
+        r.x = __builtin_amdgcn_alignbit(hi, lo, sh);
+        r.y = hi >> sh;                       // bits above 15 are not read
     } else {
         r = *reinterpret_cast<const uint4 *>(row + 16 * cg);
     }
@@ -114,10 +120,16 @@ __device__ __forceinline__ void codes_f(uint4 r, int w, float u[8]) {
         u[2] = (float)((x >> 16) & 0xffu); u[3] = (float)(x >> 24);
         u[4] = (float)(y & 0xffu);         u[5] = (float)((y >> 8) & 0xffu);
         u[6] = (float)((y >> 16) & 0xffu); u[7] = (float)(y >> 24);
-    } else {  // 6
-        const uint64_t v = (uint64_t)r.x | ((uint64_t)r.y << 32);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) u[c] = (float)(uint32_t)((v >> (6 * c)) & 63u);
+    } else {  // 6: codes 0-4 in x, code 5 across x and y, codes 6-7 in y
+        const uint32_t x = r.x, y = r.y;
+        u[0] = (float)(x & 63u);
+        u[1] = (float)((x >> 6) & 63u);
+        u[2] = (float)((x >> 12) & 63u);
+        u[3] = (float)((x >> 18) & 63u);
+        u[4] = (float)((x >> 24) & 63u);
+        u[5] = (float)(__builtin_amdgcn_alignbit(y, x, 30) & 63u);
+        u[6] = (float)((y >> 4) & 63u);
+        u[7] = (float)((y >> 10) & 63u);
     }
 }
 

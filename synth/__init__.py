@@ -132,6 +132,14 @@ WORKLOADS = {
         row_scale="f16", col_scale="f16", io="bf16", bits="fp32", pivot_frac=0.0,
         init="zero", layers=4,
         desc="the serving shape with fp32 (unquantized) state: the comparison point"),
+    "serving_int8": Workload(
+        "serving_int8", 7, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
+        row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,
+        init="zero", layers=4, desc="the serving shape with uniform 8-bit heads"),
+    "serving_int6": Workload(
+        "serving_int6", 8, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
+        row_scale="f16", col_scale="f16", io="bf16", bits="uniform6", pivot_frac=0.0,
+        init="zero", layers=4, desc="the serving shape with uniform 6-bit heads"),
     "windowed_kda": Workload(
         "windowed_kda", 5, B=512, H=32, dk=128, dv=128, T=1024, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,
