@@ -338,14 +338,8 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     float *du = reinterpret_cast<float *>(R + hd.du);
     float *dkap = reinterpret_cast<float *>(R + hd.dkap);
 
-    // Loads issued before the first barrier: the stored delta values of
-    // column t (read only by thread t) and the first (delta, 8-row block)
-    // of delta keys that this thread decays.
-    float um[kWMax];
-    if (t < DV) {
-#pragma unroll
-        for (int m = 0; m < kWMax; ++m) um[m] = m < n ? du[(size_t)m * DV + t] : 0.0f;
-    }
+    // Loaded before the first barrier: the first (delta, 8-row block) of
+    // delta keys that this thread decays.
     float kap0[8];
     {
         const int m0 = t / RG, i0 = 8 * (t - m0 * RG);
@@ -447,6 +441,13 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         sm.b.colm[c][t] = s2;
     }
     __syncthreads();
+    // the stored delta values of column t (read only by thread t), loaded
+    // once the state block is dead so that they do not add to its registers
+    float um[kWMax];
+    if (t < DV) {
+#pragma unroll
+        for (int m = 0; m < kWMax; ++m) um[m] = m < n ? du[(size_t)m * DV + t] : 0.0f;
+    }
     float w0 = 0.0f, o0 = 0.0f;
     if (t < DV) {
         w0 = col_sum<DK, DV>(sm.b, t);
