@@ -20,6 +20,8 @@ FLAGS = [
     # no packed-fp32 instructions in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # occupancy targets are hints; head sizes that cannot meet them keep fewer waves
+    "-Wno-pass-failed",
 ]
 
 

@@ -30,16 +30,24 @@ constexpr int kWMax = 16;     // window length supported by the LDS staging
 constexpr int kKMax = 1024;   // compensation entries
 constexpr int kCandMax = 1024;  // top-K candidates ranked exactly
 
-// LDS of the window-end, pack and unpack kernels.
+// LDS of the window-end, pack and unpack kernels.  The staged deltas are
+// dead once D is formed, so the entry and candidate arrays share their space.
 template <int DK, int DV>
 struct LdsW {
     Lds<DK, DV> b;            // per-step arrays (partials, row/column constants, 1/c', 1/r')
     float gn[DK];             // cumulative gate
-    alignas(16) float kst[kWMax][DK];  // decayed delta keys
-    alignas(16) float ust[kWMax][DV];  // delta values
-    uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
-    float cvl[kKMax];         // compensation value
-    uint32_t ckey[kCandMax];  // candidate keys
+    union {
+        struct {
+            alignas(16) float kst[kWMax][DK];  // decayed delta keys
+            alignas(16) float ust[kWMax][DV];  // delta values
+        };
+        struct {
+            uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
+            float cvl[kKMax];         // compensation value
+            uint32_t ckey[kCandMax];  // candidate keys
+        };
+    };
+    uint32_t cstart[DV + 1];  // old entries of column j: cstart[j] .. cstart[j+1]-1
     int red[2][8];            // block reductions
     uint32_t bc[4];           // broadcasts
 };
@@ -549,9 +557,16 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
         }
     }
     if (t < DK) sm.gn[t] = gmem[t];
-    for (int e = t; e < K; e += NT) {
-        sm.cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
-        sm.cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+    // the old entries go to LDS once the staged deltas are used up (they share
+    // the space); thread t holds entry t, and the index before it, meanwhile
+    const uint16_t *cidx = reinterpret_cast<const uint16_t *>(R + hd.cidx);
+    const float *cval = reinterpret_cast<const float *>(R + hd.cval);
+    uint32_t pe = 0, pp = 0;
+    float ve = 0.0f;
+    if (t < K) {
+        pe = cidx[t];
+        ve = cval[t];
+        pp = t > 0 ? cidx[t - 1] : 0u;
     }
     __syncthreads();
     float x[8][8];
@@ -572,6 +587,24 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
                 for (int c = 0; c < 8; ++c) x[r][c] = fma_(kq[r], uq[c], x[r][c]);
         }
     }
+    __syncthreads();  // the staged deltas are no longer read
+    // old entries into LDS, and the range of each column's entries (sorted by
+    // p = j*d_k + i)
+    if (K == 0) {
+        for (int j = t; j <= DV; j += NT) sm.cstart[j] = 0;
+    }
+    for (int e = t; e < K; e += NT) {
+        const uint32_t p = e == t ? pe : cidx[e];
+        const uint32_t q = e == t ? pp : cidx[e - 1];
+        sm.cix[e] = p;
+        sm.cvl[e] = e == t ? ve : cval[e];
+        const int j = (int)(p / DK);
+        const int jp = e > 0 ? (int)(q / DK) : -1;
+        for (int jj = jp + 1; jj <= j; ++jj) sm.cstart[jj] = e;
+        if (e == K - 1)
+            for (int jj = j + 1; jj <= DV; ++jj) sm.cstart[jj] = K;
+    }
+    __syncthreads();
     float gg[8], cc[8];
     lds_read8(&sm.gn[8 * rg], gg, 0);
     lds_read8(&sm.b.cf[8 * cg], cc, 0);
@@ -580,8 +613,9 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const uint32_t p0 = (uint32_t)((8 * cg + c) * DK + 8 * rg);
-        const int lo = lower_bound(sm.cix, K, p0);
-        for (int e = lo; e < K && sm.cix[e] < p0 + 8; ++e) {
+        const int c0 = (int)sm.cstart[8 * cg + c], c1 = (int)sm.cstart[8 * cg + c + 1];
+        const int lo = c0 + lower_bound(sm.cix + c0, c1 - c0, p0);
+        for (int e = lo; e < c1 && sm.cix[e] < p0 + 8; ++e) {
             const int rr = (int)(sm.cix[e] - p0);
             const float val = sm.cvl[e];
 #pragma unroll
@@ -606,8 +640,12 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
     if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = 0;
 }
 
+// Four waves per SIMD (128 VGPRs) for the uniform-width instantiations: the
+// few spills cost less than the lost occupancy (the window end is ~20 %
+// faster at d = 128); the per-row path would spill too much and keeps three.
 template <int DK, int DV, bool MIXED>
-__global__ void __launch_bounds__(DK * DV / 64) k_win_end(Args A) {
+__global__ void __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_eu(MIXED ? 3 : 4)))
+k_win_end(Args A) {
     constexpr int CG = DV / 8;
     __shared__ LdsW<DK, DV> sm;
     const size_t unit = blockIdx.x;
