@@ -164,6 +164,14 @@ def test_paired_heads_other_head_sizes(dk, dv):
     _run_sampled(w, 12, 64, seed=20 + dk + dv, tag=f"pairs-{dk}x{dv}")
 
 
+def test_largest_head_count():
+    """H = 4096 (the largest the layout accepts), d = 64, B = 2: 8192 states,
+    so 4-bit heads are paired across a 2,000-group table with head indices up
+    to 4095; 96 followed units over 6 steps, slot bytes compared."""
+    w = synth.WORKLOADS["serving_gdn"].with_(B=2, H=4096, dk=64, dv=64, name="serving_h4096")
+    _run_sampled(w, 6, 96, seed=31, tag="h4096")
+
+
 def test_kimi_kda_all_units_32_steps():
     """B=256 x H=32 KDA (4-bit rows + 41 FP16 pivot rows), outlier start: every unit, 32 steps."""
     _run(synth.WORKLOADS["kimi_kda"], 32, check_slots_every=16, tag="kimi-all")
