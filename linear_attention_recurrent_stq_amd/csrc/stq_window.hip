@@ -19,7 +19,8 @@
 // Thread layout as in the per-step kernel (8 x 8 block per thread, one
 // workgroup per state).  Delta keys are decayed and dotted with k and q by
 // (delta, 8-row block) pairs.  At the window end the deltas are staged in LDS
-// (window <= 16) and D is accumulated in the registers that held the base.
+// (window <= 16) and D is accumulated in the state block's registers while
+// the base codes wait in theirs.
 #include "stq_device.h"
 
 namespace stq {
