@@ -238,6 +238,8 @@ __device__ __forceinline__ float row_max(const Lds<DK, DV> &sm, int i) {
 struct Rows {
     int w[8];        // width of each of the thread's rows
     uint32_t ro[8];  // byte offset of each row inside the head region
+    uint32_t m8;     // kW4P: pivot bits of the thread's 8 rows (w and ro unused)
+    uint32_t base;   // kW4P: byte offset of the thread's first row
 };
 
 // W: the head's uniform row width (32: fp32 rows), or 0 / kW4P for per-row
@@ -245,8 +247,32 @@ struct Rows {
 template <int W>
 constexpr bool per_row() { return W == 0 || W == kW4P; }
 
+// kW4P heads: the pivot bits of key rows [32 j, 32 j + 32) for a per-thread j.
+__device__ __forceinline__ uint32_t pivot_word(const HeadDesc &hd, int j) {
+    const uint32_t m0 = hd.pmask[0], m1 = hd.pmask[1], m2 = hd.pmask[2], m3 = hd.pmask[3];
+    return j == 0 ? m0 : j == 1 ? m1 : j == 2 ? m2 : m3;
+}
+
+// kW4P heads: the pivot bits of the thread's rows 8 rg .. 8 rg + 7, and the
+// byte offset of row 8 rg (4-bit rows take d_v/2 bytes, pivot rows 2 d_v).
+template <int DV>
+__device__ __forceinline__ uint32_t pivot_block(const HeadDesc &hd, int rg, uint32_t &base) {
+    const int i = 8 * rg, j = i >> 5, sh = i & 31;
+    const uint32_t wj = pivot_word(hd, j);
+    uint32_t before = __builtin_popcount(wj & ((1u << sh) - 1u));
+#pragma unroll
+    for (int k = 0; k < 3; ++k) before += k < j ? __builtin_popcount(hd.pmask[k]) : 0u;
+    base = (uint32_t)i * (DV / 2) + before * (3 * DV / 2);
+    return (wj >> sh) & 0xffu;
+}
+
 template <int DV, int W>
 __device__ __forceinline__ void row_geometry(const Args &A, const HeadDesc &hd, int rg, Rows &rw) {
+    if (W == kW4P) {
+        // kept as a mask and one offset; row_w and row_o derive the rest
+        rw.m8 = pivot_block<DV>(hd, rg, rw.base);
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         if (!per_row<W>()) {
@@ -260,9 +286,22 @@ __device__ __forceinline__ void row_geometry(const Args &A, const HeadDesc &hd, 
     }
 }
 
-// Width of key row i of the head (uniform width or the row table).
+// Width and byte offset of the thread's row r.
+template <int W>
+__device__ __forceinline__ int row_w(const Rows &rw, int r) {
+    return W == kW4P ? ((rw.m8 >> r) & 1u ? 16 : 4) : rw.w[r];
+}
+template <int DV, int W>
+__device__ __forceinline__ uint32_t row_o(const Rows &rw, int r) {
+    if (W != kW4P) return rw.ro[r];
+    const uint32_t piv_before = __builtin_popcount(rw.m8 & ((1u << r) - 1u));
+    return rw.base + (uint32_t)r * (DV / 2) + piv_before * (3 * DV / 2);
+}
+
+// Width of key row i of the head (uniform width, the pivot mask or the row table).
 template <int W>
 __device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i) {
+    if (W == kW4P) return (pivot_word(hd, i >> 5) >> (i & 31)) & 1u ? 16 : 4;
     return !per_row<W>() ? W : (int)row_width(A.rows[hd.rows + i]);
 }
 
@@ -320,7 +359,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                if (rw.w[r] != 16) m = fmaxf(m, fabsf(x[r][c]));
+                if (row_w<W>(rw, r) != 16) m = fmaxf(m, fabsf(x[r][c]));
             sm.colm[c][t] = m;
         }
     }
@@ -347,11 +386,11 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             if (W == 32) {
-                float4 *p = reinterpret_cast<float4 *>(R + rw.ro[r] + 32 * cg);
+                float4 *p = reinterpret_cast<float4 *>(R + row_o<DV, W>(rw, r) + 32 * cg);
                 p[0] = make_float4(x[r][0], x[r][1], x[r][2], x[r][3]);
                 p[1] = make_float4(x[r][4], x[r][5], x[r][6], x[r][7]);
             } else {
-                store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
+                store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece(x[r]));
             }
         }
         return;
@@ -362,7 +401,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         float m = 0.0f;
-        if (rw.w[r] != 16) {
+        if (row_w<W>(rw, r) != 16) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float z = x[r][c] * icc[c];
@@ -403,14 +442,14 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         // a row step saturated at 65504: clamp codes to +-qmax
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
-            else quant_row<true>(R + rw.ro[r], cg, rw.w[r], fabsf(irr[r]), x[r]);
+            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece(x[r]));
+            else quant_row<true>(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r), fabsf(irr[r]), x[r]);
         }
     } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if (rw.w[r] == 16) store_piece(R + rw.ro[r], cg, 16, pivot_piece(x[r]));
-            else quant_row<false>(R + rw.ro[r], cg, rw.w[r], irr[r], x[r]);
+            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece(x[r]));
+            else quant_row<false>(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r), irr[r], x[r]);
         }
     }
 }

@@ -182,10 +182,13 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
                 const int b = keyrow ? L->bits[(size_t)h * dk + i] : L->bits[h];
                 w4p &= b == 4 || b == 16;
             }
-            if (w4p) d.width = stq::kW4P;
+            if (w4p) {
+                d.width = stq::kW4P;
+                for (int i = 0; i < dk; ++i)
+                    if (L->bits[(size_t)h * dk + i] == 16) d.pmask[i / 32] |= 1u << (i % 32);
+            }
             L->step_mix = w4p ? (L->step_mix > 1 ? 2 : 1) : 2;
         }
-        d.cbytes = (uint32_t)p;
         p = up(p, 16);
         if (nq > 0) {
             d.rs = (uint32_t)p;

@@ -26,8 +26,8 @@ struct HeadDesc {
     uint16_t width;    // width shared by every row (4/6/8/16); kW4P: 4-bit rows and
                        // FP16 pivot rows; 0: rows of other differing widths
     uint16_t nquant;   // number of quantized (non-pivot) rows
-    uint32_t cbytes;   // bytes of the code rows (a multiple of 16)
-    uint32_t pad[3];
+    uint32_t pmask[4]; // kW4P heads: bit i % 32 of word i / 32 set if key row i is an
+                       // FP16 pivot row (the row offsets follow from it); else 0
 };
 static_assert(sizeof(HeadDesc) == 64, "HeadDesc is 64 bytes");
 

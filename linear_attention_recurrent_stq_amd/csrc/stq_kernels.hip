@@ -56,7 +56,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         // fp32 rows: the 8 values of each row piece straight into the block
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float4 *p = reinterpret_cast<const float4 *>(R + rw.ro[r] + 32 * cg);
+            const float4 *p = reinterpret_cast<const float4 *>(R + row_o<DV, W>(rw, r) + 32 * cg);
             const float4 a0 = p[0], a1 = p[1];
             x[r][0] = a0.x; x[r][1] = a0.y; x[r][2] = a0.z; x[r][3] = a0.w;
             x[r][4] = a1.x; x[r][5] = a1.y; x[r][6] = a1.z; x[r][7] = a1.w;
@@ -68,16 +68,16 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             raw[r] = make_uint4(0, 0, 0, 0);
-            if (rw.w[r] != 16) {
-                raw[r].x = *reinterpret_cast<const uint32_t *>(R + rw.ro[r] + 4 * cg);
+            if (row_w<W>(rw, r) != 16) {
+                raw[r].x = *reinterpret_cast<const uint32_t *>(R + row_o<DV, W>(rw, r) + 4 * cg);
             } else if (pr < 0) {
-                pv = load_piece(R + rw.ro[r], cg, 16);
+                pv = load_piece(R + row_o<DV, W>(rw, r), cg, 16);
                 pr = r;
             }
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + rw.ro[r], cg, rw.w[r]);
+        for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r));
     }
 
     // per key row and per value column constants, computed once per state
@@ -132,7 +132,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int i = 8 * rg + r;
-            const int w = rw.w[r];
+            const int w = row_w<W>(rw, r);
             if (W == 32) {
                 const float a = sm.af[i];
 #pragma unroll
@@ -140,7 +140,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             } else if (w == 16) {
                 const float a = sm.af[i];
                 // kW4P: a second pivot row of the block is loaded here (rare)
-                const uint4 pc = W != kW4P ? raw[r] : r == pr ? pv : load_piece(R + rw.ro[r], cg, 16);
+                const uint4 pc = W != kW4P ? raw[r] : r == pr ? pv : load_piece(R + row_o<DV, W>(rw, r), cg, 16);
                 const uint32_t hv[4] = {pc.x, pc.y, pc.z, pc.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {

@@ -80,7 +80,7 @@ def test_mixed_row_widths_d64():
     _run(w, 20, bits=bits, check_slots_every=5, tag="kda-mixed")
 
 
-def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None):
+def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None, bits=None):
     """Full batch on the GPU; n_units seeded (request, head) units (or the
     given list) followed by the oracle over T steps (the others keep their
     first inputs)."""
@@ -92,7 +92,7 @@ def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None)
     follow = sorted(follow)
     print(f"[{tag}] {w.name} layer {layer}: {len(follow)} followed units of B={w.B} x H={w.H}, "
           f"T={T}", flush=True)
-    hs = _harness(w, layer=layer, follow=follow)
+    hs = _harness(w, layer=layer, follow=follow, bits=bits)
     try:
         if track:
             hs.track_fp32()
@@ -162,6 +162,68 @@ def test_paired_heads_other_head_sizes(dk, dv):
     sizes: 64 followed units over 12 steps, slot bytes compared at the end."""
     w = synth.WORKLOADS["serving_gdn"].with_(B=256, dk=dk, dv=dv, name=f"serving_{dk}x{dv}")
     _run_sampled(w, 12, 64, seed=20 + dk + dv, tag=f"pairs-{dk}x{dv}")
+
+
+def _both_kinds_bits(d):
+    """Eight KDA heads: 4-bit rows with FP16 pivot rows (blocks of 8 rows
+    holding 0 to 8 pivots), heads of 4-bit rows only, and an all-pivot head."""
+    bits = np.full((8, d), 4, np.uint8)
+    bits[0, [0, 1, 9, 12, 13, 14, 40, d - 1]] = 16
+    bits[1, 5] = 16
+    bits[3, :] = 16
+    bits[4, [2, 3, 4, d // 2, d - 3]] = 16
+    bits[5, d - 1] = 16
+    bits[7, 8:16] = 16
+    return bits
+
+
+def _expected_groups(bits):
+    """Heads whose rows are all 4-bit in pairs, in head order; every other
+    head alone; an unpaired 4-bit head last."""
+    groups, pending = [], None
+    for h, r in enumerate(bits):
+        if not (r == 4).all():
+            groups.append((h, 0xFFFF))
+        elif pending is None:
+            pending = h
+        else:
+            groups.append((pending, h))
+            pending = None
+    if pending is not None:
+        groups.append((pending, 0xFFFF))
+    return groups
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_pivot_row_heads_in_a_paired_batch(d):
+    """A batch large enough for paired heads (1024 x 8 states) of KDA heads
+    with 4-bit and FP16 pivot rows (pivot masks and head groups read back from
+    the pool header), 4-bit heads (paired) and an all-pivot head: every head
+    of 3 requests followed over 12 steps from the outlier start, slot bytes
+    compared."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["kimi_kda"].with_(B=1024, H=8, dk=d, dv=d, name=f"kda_pairs_d{d}")
+    bits = _both_kinds_bits(d)
+    L = stq.Layout.from_workload(w, bits.ravel())
+    pool = stq.Pool(L, 1)
+    hdr = pool.buffer[:L.header_bytes].cpu().numpy()
+    desc = hdr[:64 * w.H].view(np.uint32).reshape(w.H, 16)
+    for h in range(w.H):
+        r = bits[h]
+        w4p = np.isin(r, (4, 16)).all() and (r == 4).any() and (r == 16).any()
+        want = np.zeros(4, np.uint32)
+        if w4p:
+            for i in np.nonzero(r == 16)[0]:
+                want[i // 32] |= np.uint32(1 << (i % 32))
+        assert (desc[h, 12:16] == want).all(), f"pivot mask of head {h}"
+    want = _expected_groups(bits)
+    g0 = 64 * w.H + 4 * w.H * d
+    got = hdr[g0:g0 + 4 * len(want)].view(np.uint32)
+    assert [(int(x) & 0xFFFF, int(x) >> 16) for x in got] == want
+    del pool
+    follow = [(b, h) for b in (0, 517, 1023) for h in range(w.H)]
+    _run_sampled(w, 12, 0, seed=0, follow=follow, bits=bits.ravel(), tag=f"pairs-4p-d{d}")
 
 
 def test_largest_head_count():
