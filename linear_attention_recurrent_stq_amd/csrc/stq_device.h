@@ -60,10 +60,68 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     return x;
 }
 
-__device__ __forceinline__ float load1(const void *p, int bf16, size_t e) {
-    if (bf16) return __uint_as_float((uint32_t)(static_cast<const uint16_t *>(p)[e]) << 16);
-    return static_cast<const float *>(p)[e];
+// Values whose type is chosen at run time (bf16 or fp32 inputs, fp16 or fp32
+// scales) are read as the dword holding the element (ld_dword) and converted
+// afterwards (dec_io, dec_scale, with the element index's parity).  No load
+// then sits in a branch of its own: a load used inside a branch is waited for
+// there, which would serialise a state's input loads one round trip each.
+// Every such array has an even number of elements and a 4-byte aligned start,
+// so the dword lies inside it.
+__device__ __forceinline__ uint32_t ld_dword(const void *p, int half, size_t e) {
+    return *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p) + (half ? (e >> 1) * 4 : e * 4));
 }
+// bf16 (if bf16) or fp32 input element of index parity `odd`
+__device__ __forceinline__ float dec_io(uint32_t d, int bf16, int odd) {
+    const uint32_t h = odd ? (d & 0xffff0000u) : (d << 16);
+    return __uint_as_float(bf16 ? h : d);
+}
+// fp16 (if f16) or fp32 scale of index parity `odd`
+__device__ __forceinline__ float dec_scale(uint32_t d, int f16, int odd) {
+    return f16 ? f16v(odd ? d >> 16 : d) : __uint_as_float(d);
+}
+__device__ __forceinline__ float load1(const void *p, int bf16, size_t e) {
+    return dec_io(ld_dword(p, bf16, e), bf16, (int)(e & 1));
+}
+
+// The per-state inputs thread t reads, for key row t (t < d_k) and value
+// column t (t < d_v), as raw dwords.  Threads past d_k or d_v read element 0
+// and do not use it, so the loads need no branch.
+struct Inputs {
+    float a, beta;
+    uint32_t r, k, q;  // key row t: row scale, key, query
+    uint32_t c, v;     // value column t: column scale, value
+};
+
+// A use of every input dword on all threads, placed once they have been
+// used: the loads then cannot be moved into the branches that use them (which
+// would issue them late, behind loads meant to be in flight longer).
+__device__ __forceinline__ void keep_inputs(const Inputs &p) {
+    asm volatile("" ::"v"(p.a), "v"(p.beta), "v"(p.r), "v"(p.k), "v"(p.q), "v"(p.c), "v"(p.v));
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void fetch_inputs(const Args &A, const HeadDesc &hd, const uint8_t *R, size_t unit,
+                                             int t, Inputs &p) {
+    const int tk = t < DK ? t : 0, tv = t < DV ? t : 0;
+    p.beta = A.beta[unit];
+    p.a = A.a[A.gate_vec ? unit * DK + tk : unit];
+    // a head without scales has offset 0 here: still inside its region
+    p.r = ld_dword(R + hd.rs, A.rs16, tk);
+    p.k = ld_dword(A.k, A.io_bf16, unit * DK + tk);
+    p.q = ld_dword(A.q, A.io_bf16, unit * DK + tk);
+    p.c = ld_dword(R + hd.cs, 1, tv);
+    p.v = ld_dword(A.v, A.io_bf16, unit * DV + tv);
+}
+
+// A head's width and quantized-row count share one descriptor dword; reading
+// the dword keeps the load on the scalar unit (no 16-bit scalar loads).
+__device__ __forceinline__ uint32_t head_wq(const HeadDesc &hd) {
+    static_assert(offsetof(HeadDesc, width) == 44 && offsetof(HeadDesc, nquant) == 46,
+                  "width and nquant share the 12th dword");
+    return reinterpret_cast<const uint32_t *>(&hd)[11];
+}
+__device__ __forceinline__ int head_width(const HeadDesc &hd) { return (int)(head_wq(hd) & 0xffffu); }
+__device__ __forceinline__ int head_nquant(const HeadDesc &hd) { return (int)(head_wq(hd) >> 16); }
 
 // The piece of a row owned by column group cg: 8 codes of w bits = w bytes.
 __device__ __forceinline__ uint4 load_piece(const uint8_t *row, int cg, int w) {
@@ -308,7 +366,7 @@ __device__ __forceinline__ int width_of(const Args &A, const HeadDesc &hd, int i
 // Whether the head has quantized rows: known from the width unless rows differ.
 template <int W>
 __device__ __forceinline__ bool has_quant(const HeadDesc &hd) {
-    return (W == 16 || W == 32) ? false : (!per_row<W>() ? true : hd.nquant > 0);
+    return (W == 16 || W == 32) ? false : (!per_row<W>() ? true : head_nquant(hd) > 0);
 }
 
 template <int N>

@@ -10,12 +10,9 @@ namespace {
 // ----------------------------------------------------------------- step
 
 // The inputs of a 4-bit state that a workgroup fetches ahead of its compute:
-// for thread t, the code piece of each of its 8 rows, the inputs of key row t
-// (t < d_k) and of value column t (t < d_v).
+// for thread t, the code piece of each of its 8 rows and its Inputs.
 struct Pre4 {
-    float a, r, k, q;  // key row t: gate, row scale, key, query
-    float c, v;        // value column t: column scale, value
-    float beta;
+    Inputs in;
     uint32_t raw[8];
 };
 
@@ -25,18 +22,7 @@ __device__ __forceinline__ void fetch4(const Args &A, const HeadDesc &hd, const 
     const uint8_t *base = R + (uint32_t)(8 * rg * (DV / 2) + 4 * cg);
 #pragma unroll
     for (int r = 0; r < 8; ++r) p.raw[r] = *reinterpret_cast<const uint32_t *>(base + r * (DV / 2));
-    p.beta = A.beta[unit];
-    if (t < DK) {
-        p.a = A.gate_vec ? A.a[unit * DK + t] : A.a[unit];
-        p.r = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[t])
-                     : reinterpret_cast<const float *>(R + hd.rs)[t];
-        p.k = load1(A.k, A.io_bf16, unit * DK + t);
-        p.q = load1(A.q, A.io_bf16, unit * DK + t);
-    }
-    if (t < DV) {
-        p.c = A.cs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
-        p.v = load1(A.v, A.io_bf16, unit * DV + t);
-    }
+    fetch_inputs<DK, DV>(A, hd, R, unit, t, p.in);
 }
 
 // One state.  PRE: a 4-bit state whose inputs were fetched into p (W == 4);
@@ -81,45 +67,29 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     }
 
     // per key row and per value column constants, computed once per state
-    float beta, vv = 0.0f;
-    if (PRE) {
-        beta = p.beta;
-        if (t < DK) {
-            const float g = p.a * p.r;
-            sm.g[t] = g;
-            sm.g16[t] = g * 0.0625f;
-            sm.nog[t] = -8.0f * g;
-            sm.af[t] = p.a;
-            sm.kf[t] = p.k;
-            sm.qf[t] = p.q;
-        }
-        if (t < DV) {
-            sm.cf[t] = p.c;
-            vv = p.v;
-        }
-    } else {
-        beta = A.beta[unit];
-        if (t < DK) {
-            const int i = t;
-            const int w = width_of<W>(A, hd, i);
-            const float a = A.gate_vec ? A.a[unit * DK + i] : A.a[unit];
-            float ri = 0.0f;
-            if (quant && w != 16)
-                ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[i])
-                            : reinterpret_cast<const float *>(R + hd.rs)[i];
-            const float g = a * ri;
-            sm.g[i] = g;
-            sm.g16[i] = g * 0.0625f;
-            sm.nog[i] = w < 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
-            sm.af[i] = a;
-            sm.kf[i] = load1(A.k, A.io_bf16, unit * DK + i);
-            sm.qf[i] = load1(A.q, A.io_bf16, unit * DK + i);
-        }
-        if (t < DV) {
-            sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
-            vv = load1(A.v, A.io_bf16, unit * DV + t);
-        }
+    Inputs own;
+    if (!PRE) fetch_inputs<DK, DV>(A, hd, R, unit, t, own);
+    const Inputs &in = PRE ? p.in : own;
+    const float beta = in.beta;
+    float vv = 0.0f;
+    if (t < DK) {
+        const int w = width_of<W>(A, hd, t);
+        const float rl = dec_scale(in.r, A.rs16, t & 1);
+        const float ri = (quant && w != 16) ? rl : 0.0f;
+        const float g = in.a * ri;
+        sm.g[t] = g;
+        sm.g16[t] = g * 0.0625f;
+        sm.nog[t] = w < 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
+        sm.af[t] = in.a;
+        sm.kf[t] = dec_io(in.k, A.io_bf16, t & 1);
+        sm.qf[t] = dec_io(in.q, A.io_bf16, t & 1);
     }
+    if (t < DV) {
+        const float c = dec_scale(in.c, 1, t & 1);
+        sm.cf[t] = (quant && A.cs16) ? c : 1.0f;
+        vv = dec_io(in.v, A.io_bf16, t & 1);
+    }
+    keep_inputs(in);
     __syncthreads();
     // decay + dequantize: A_ij, row by row, with the w = (a.S) k column
     // partial sums over the thread's 8 rows accumulated as the rows come in.
@@ -223,6 +193,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
         const size_t u2 = (size_t)b * A.H + h2;
         Pre4 p1, p2;
         fetch4<DK, DV>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the first state's loads ahead
         fetch4<DK, DV>(A, hd2, S + hd2.off, u2, t, rg, cg, p2);
         step_tile<DK, DV, 4, true>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
         step_tile<DK, DV, 4, true>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
@@ -230,7 +201,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
     }
     uint8_t *R = S + hd1.off;
     Pre4 none;
-    switch (hd1.width) {
+    switch (head_width(hd1)) {
         case 4: step_tile<DK, DV, 4, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 6: step_tile<DK, DV, 6, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case 8: step_tile<DK, DV, 8, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
@@ -276,7 +247,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_pack(Args A) {
     if (slot < 0 || slot >= A.nslots) return;
     const HeadDesc hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
-    switch (hd.width) {
+    switch (head_width(hd)) {
         case 4: pack_tile<DK, DV, 4>(A, hd, R, sm, t, rg, cg, unit); break;
         case 6: pack_tile<DK, DV, 6>(A, hd, R, sm, t, rg, cg, unit); break;
         case 8: pack_tile<DK, DV, 8>(A, hd, R, sm, t, rg, cg, unit); break;
@@ -307,7 +278,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_unpack(Args A) {
     const uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     Rows rw;
     row_geometry<DV, 0>(A, hd, rg, rw);
-    const bool quant = hd.nquant > 0;
+    const bool quant = head_nquant(hd) > 0;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int i = 8 * rg + r;

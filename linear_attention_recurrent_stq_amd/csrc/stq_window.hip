@@ -308,21 +308,31 @@ __device__ __forceinline__ void base_block(const Rows &rw, const uint4 (&raw)[8]
 // Row and column constants of the base dequantization (row scale r: in g,
 // r/16 in g16, -2^(w-1) r in nog; column scales in cf).
 template <int DK, int DV, int W>
-__device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd, const uint8_t *R,
+__device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd, uint32_t rraw, uint32_t craw,
                                                Lds<DK, DV> &sm, int t) {
     const bool quant = has_quant<W>(hd);
     if (t < DK) {
         const int w = width_of<W>(A, hd, t);
-        float ri = 0.0f;
-        if (quant && w != 16)
-            ri = A.rs16 ? f16v(reinterpret_cast<const uint16_t *>(R + hd.rs)[t])
-                        : reinterpret_cast<const float *>(R + hd.rs)[t];
+        const float rl = dec_scale(rraw, A.rs16, t & 1);
+        const float ri = (quant && w != 16) ? rl : 0.0f;
         sm.g[t] = ri;
         sm.g16[t] = ri * 0.0625f;
         sm.nog[t] = w != 16 ? -(float)(1 << (w - 1)) * ri : 0.0f;
     }
-    if (t < DV)
-        sm.cf[t] = (quant && A.cs16) ? f16v(reinterpret_cast<const uint16_t *>(R + hd.cs)[t]) : 1.0f;
+    if (t < DV) {
+        const float c = dec_scale(craw, 1, t & 1);
+        sm.cf[t] = (quant && A.cs16) ? c : 1.0f;
+    }
+}
+
+// The same from the head's stored scales (a head without scales has offset 0
+// here: still inside its region).
+template <int DK, int DV, int W>
+__device__ __forceinline__ void base_constants(const Args &A, const HeadDesc &hd, const uint8_t *R,
+                                               Lds<DK, DV> &sm, int t) {
+    const uint32_t rraw = ld_dword(R + hd.rs, A.rs16, t < DK ? t : 0);
+    const uint32_t craw = ld_dword(R + hd.cs, 1, t < DV ? t : 0);
+    base_constants<DK, DV, W>(A, hd, rraw, craw, sm, t);
 }
 
 template <int DK, int DV, int W>
@@ -330,14 +340,11 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
                                          LdsWin<DK, DV> &sm, uint32_t *cix, float *cvl, float *kge, float *qge,
                                          int t, int rg, int cg) {
     constexpr int NT = DK * DV / 64, RG = DK / 8;
-    const int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
     const int W_ = A.window;
-    if (n < 0 || n >= W_) {
-        // a delta count outside [0, W) is not a state this library wrote
-        if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
-        return;
-    }
     const int K = A.comps;
+    // Every load below stays inside the head region whatever the delta
+    // count, so they are all issued before the count arrives (no load waits
+    // for another).
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
     uint4 raw[8];
@@ -347,12 +354,13 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     float *du = reinterpret_cast<float *>(R + hd.du);
     float *dkap = reinterpret_cast<float *>(R + hd.dkap);
 
-    // Loaded before the first barrier: the first (delta, 8-row block) of
-    // delta keys that this thread decays.
+    // the first (delta, 8-row block) of delta keys that this thread decays
+    // (used only if that delta exists)
     float kap0[8];
+    const int m0 = t / RG;
     {
-        const int m0 = t / RG, i0 = 8 * (t - m0 * RG);
-        if (m0 < n) {
+        const int i0 = 8 * (t - m0 * RG);
+        if (m0 < W_) {
             const float4 *p = reinterpret_cast<const float4 *>(dkap + (size_t)m0 * DK + i0);
             const float4 a0 = p[0], a1 = p[1];
             kap0[0] = a0.x; kap0[1] = a0.y; kap0[2] = a0.z; kap0[3] = a0.w;
@@ -360,27 +368,53 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         }
     }
 
-    // per key row / value column constants
-    base_constants<DK, DV, W>(A, hd, R, sm.b, t);
-    const float beta = A.beta[unit];
-    float vv = 0.0f;
+    // per key row / value column inputs and constants
+    Inputs in;
+    fetch_inputs<DK, DV>(A, hd, R, unit, t, in);
+    const float gold = gmem[t < DK ? t : 0];
+    // this thread's first compensation entry (more below if K > NT)
+    const uint16_t *cidx = reinterpret_cast<const uint16_t *>(R + hd.cidx);
+    const float *cval = reinterpret_cast<const float *>(R + hd.cval);
+    uint32_t ci0 = 0;
+    float cv0 = 0.0f;
+    if (t < K) {
+        ci0 = cidx[t];
+        cv0 = cval[t];
+    }
+    const int n = *reinterpret_cast<const int32_t *>(R + hd.wn);
+    base_constants<DK, DV, W>(A, hd, in.r, in.c, sm.b, t);
+    const float beta = in.beta;
+    float vv = 0.0f, gnew = 0.0f;
     if (t < DK) {
-        const float a = A.gate_vec ? A.a[unit * DK + t] : A.a[unit];
-        const float k = load1(A.k, A.io_bf16, unit * DK + t);
-        const float q = load1(A.q, A.io_bf16, unit * DK + t);
-        const float g = gmem[t] * a;
+        const float a = in.a;
+        const float k = dec_io(in.k, A.io_bf16, t & 1);
+        const float q = dec_io(in.q, A.io_bf16, t & 1);
+        const float g = gold * a;
         sm.b.af[t] = a;
         sm.kr[t] = k;
         sm.qr[t] = q;
         sm.b.kf[t] = g * k;
         sm.b.qf[t] = g * q;
-        gmem[t] = g;
+        gnew = g;
     }
-    if (t < DV) vv = load1(A.v, A.io_bf16, unit * DV + t);
-    for (int e = t; e < K; e += NT) {
-        cix[e] = reinterpret_cast<const uint16_t *>(R + hd.cidx)[e];
-        cvl[e] = reinterpret_cast<const float *>(R + hd.cval)[e];
+    if (t < DV) vv = dec_io(in.v, A.io_bf16, t & 1);
+    if (t < K) {
+        cix[t] = ci0;
+        cvl[t] = cv0;
     }
+    keep_inputs(in);
+    asm volatile("" ::"v"(gold), "v"(ci0), "v"(cv0));  // (as keep_inputs)
+    for (int e = t + NT; e < K; e += NT) {
+        cix[e] = cidx[e];
+        cvl[e] = cval[e];
+    }
+    if (n < 0 || n >= W_) {
+        // a delta count outside [0, W) is not a state this library wrote:
+        // nothing is stored into it
+        if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
+        return;
+    }
+    if (t < DK) gmem[t] = gnew;
     __syncthreads();
 
     // column ranges of the entries (sorted by p = j*d_k + i), and each
@@ -658,7 +692,7 @@ k_win_end(Args A) {
     const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     if (*reinterpret_cast<const int32_t *>(R + hd.wn) != A.window) return;
-    switch (hd.width) {
+    switch (head_width(hd)) {
         case 4: end_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
         case 6: end_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
         case 8: end_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
@@ -689,7 +723,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     }
     const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
-    switch (hd.width) {
+    switch (head_width(hd)) {
         case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
         case 6: win_tile<DK, DV, 6>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
         case 8: win_tile<DK, DV, 8>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
@@ -740,7 +774,7 @@ __global__ void __launch_bounds__(DK * DV / 64) k_pack_win(Args A) {
     if (slot < 0 || slot >= A.nslots) return;
     const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
-    switch (hd.width) {
+    switch (head_width(hd)) {
         case 4: pack_win_tile<DK, DV, 4>(A, hd, R, unit, sm, t, rg, cg); break;
         case 6: pack_win_tile<DK, DV, 6>(A, hd, R, unit, sm, t, rg, cg); break;
         case 8: pack_win_tile<DK, DV, 8>(A, hd, R, unit, sm, t, rg, cg); break;
