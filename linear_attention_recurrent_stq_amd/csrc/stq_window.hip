@@ -342,9 +342,8 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     constexpr int NT = DK * DV / 64, RG = DK / 8;
     const int W_ = A.window;
     const int K = A.comps;
-    // Every load below stays inside the head region whatever the delta
-    // count, so they are all issued before the count arrives (no load waits
-    // for another).
+    // The loads below do not depend on the delta count, so they are all
+    // issued before it arrives (no load waits for another).
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
     uint4 raw[8];
@@ -353,20 +352,6 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
     float *gmem = reinterpret_cast<float *>(R + hd.g);
     float *du = reinterpret_cast<float *>(R + hd.du);
     float *dkap = reinterpret_cast<float *>(R + hd.dkap);
-
-    // the first (delta, 8-row block) of delta keys that this thread decays
-    // (used only if that delta exists)
-    float kap0[8];
-    const int m0 = t / RG;
-    {
-        const int i0 = 8 * (t - m0 * RG);
-        if (m0 < W_) {
-            const float4 *p = reinterpret_cast<const float4 *>(dkap + (size_t)m0 * DK + i0);
-            const float4 a0 = p[0], a1 = p[1];
-            kap0[0] = a0.x; kap0[1] = a0.y; kap0[2] = a0.z; kap0[3] = a0.w;
-            kap0[4] = a1.x; kap0[5] = a1.y; kap0[6] = a1.z; kap0[7] = a1.w;
-        }
-    }
 
     // per key row / value column inputs and constants
     Inputs in;
@@ -415,6 +400,18 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         return;
     }
     if (t < DK) gmem[t] = gnew;
+    // the first (delta, 8-row block) of delta keys that this thread decays,
+    // in flight across the barrier (the delta count is known by now)
+    float kap0[8];
+    {
+        const int m0 = t / RG, i0 = 8 * (t - m0 * RG);
+        if (m0 < n) {
+            const float4 *p = reinterpret_cast<const float4 *>(dkap + (size_t)m0 * DK + i0);
+            const float4 a0 = p[0], a1 = p[1];
+            kap0[0] = a0.x; kap0[1] = a0.y; kap0[2] = a0.z; kap0[3] = a0.w;
+            kap0[4] = a1.x; kap0[5] = a1.y; kap0[6] = a1.z; kap0[7] = a1.w;
+        }
+    }
     __syncthreads();
 
     // column ranges of the entries (sorted by p = j*d_k + i), and each
