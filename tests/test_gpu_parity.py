@@ -226,6 +226,15 @@ def test_pivot_row_heads_in_a_paired_batch(d):
     _run_sampled(w, 12, 0, seed=0, follow=follow, bits=bits.ravel(), tag=f"pairs-4p-d{d}")
 
 
+def test_paired_heads_fp32_inputs_and_scales():
+    """Paired 4-bit heads (256 x 32 states) with fp32 q/k/v, fp32 row scales
+    and no column scales: the other input and scale types on the prefetch
+    path; 64 followed units over 10 steps, slot bytes compared."""
+    w = synth.WORKLOADS["serving_gdn"].with_(B=256, io="f32", row_scale="f32", col_scale="none",
+                                             name="serving_f32_io")
+    _run_sampled(w, 10, 64, seed=41, tag="pairs-f32")
+
+
 def test_largest_head_count():
     """H = 4096 (the largest the layout accepts), d = 64, B = 2: 8192 states,
     so 4-bit heads are paired across a 2,000-group table with head indices up
