@@ -148,6 +148,29 @@ stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids
 stq_status stq_pack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
                     const float *d_state, void *stream);
 
+/*
+ * Lifetime-aware bit allocation (host only; STEPQuant essay, temporal-axis
+ * paragraphs and the Proposition 1 discussion: an error that the update does
+ * not remove fades only by the gate, so long-lived units get more bits within
+ * a fixed average, and the riskiest few stay FP16 pivots).  Fills unit_bits
+ * for stq_config.unit_bits from per-unit calibration statistics:
+ *   n_units      units of one layer: H (per head) or H*d_k (per key row)
+ *   gate_mean    [n_units] host, mean gate of the unit, in [0, 1]
+ *   state_msq    [n_units] host, mean squared state entry of the unit, >= 0
+ *   avg_bits     mean width over the non-pivot units, in [4, 8]
+ *   n_pivots     units kept as FP16 pivots (width 16), in [0, n_units]
+ *   unit_bits    [n_units] host output: 4, 6, 8 or 16
+ * Weight s = state_msq / (1 - min(gate_mean, 1 - 2^-20)); the n_pivots largest
+ * weights become pivots; the others start at 4 and, while 2 more bits fit in
+ * floor(avg_bits * (n_units - n_pivots)), the unit with the largest
+ * s * (4^-b - 4^-(b+2)) gains 2 bits (ties: lower index), up to 8.  Double
+ * arithmetic; deterministic.  Errors: STQ_ERR_INVALID (NULL, n_units < 1,
+ * avg_bits or n_pivots out of range, a statistic out of range or not finite);
+ * nothing is written then.
+ */
+stq_status stq_allocate_bits(int32_t n_units, const float *gate_mean, const float *state_msq,
+                             double avg_bits, int32_t n_pivots, uint8_t *unit_bits);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ NONE, F32, F16, BF16 = 0, 1, 2, 3
 
 SYMBOLS = ["stq_status_string", "stq_last_error", "stq_pack_layout", "stq_layout_query",
            "stq_layout_head", "stq_layout_free", "stq_alloc_pool", "stq_decode_step",
-           "stq_unpack", "stq_pack"]
+           "stq_unpack", "stq_pack", "stq_allocate_bits"]
 
 
 class StqConfig(C.Structure):
@@ -61,8 +61,9 @@ _lib.stq_alloc_pool.argtypes = [_P, C.c_int32, _P, C.c_size_t, _P, C.POINTER(Stq
 _lib.stq_decode_step.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.stq_unpack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
 _lib.stq_pack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
+_lib.stq_allocate_bits.argtypes = [C.c_int32, _P, _P, C.c_double, C.c_int32, _P]
 for _f in ("stq_pack_layout", "stq_layout_query", "stq_layout_head", "stq_alloc_pool",
-           "stq_decode_step", "stq_unpack", "stq_pack"):
+           "stq_decode_step", "stq_unpack", "stq_pack", "stq_allocate_bits"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -206,3 +207,18 @@ def pack(pool: Pool, slot_ids, state, stream=None) -> None:
         raise ValueError("state must be [B,H,d_k,d_v]")
     _check(_lib.stq_pack(C.byref(pool.pool), B, _dptr(slot_ids, "slot_ids", torch.int32),
                          _dptr(state, "state", torch.float32), _stream_ptr(stream)), "stq_pack")
+
+
+def allocate_bits(gate_mean, state_msq, avg_bits: float, n_pivots: int):
+    """stq_allocate_bits on host arrays (one entry per unit); returns the
+    uint8 unit widths (4/6/8, 16 for pivots) for Layout / stq_config."""
+    import numpy as np
+    g = np.ascontiguousarray(gate_mean, dtype=np.float32)
+    m = np.ascontiguousarray(state_msq, dtype=np.float32)
+    if g.ndim != 1 or g.shape != m.shape:
+        raise ValueError("gate_mean and state_msq must be 1-D of one length")
+    out = np.zeros(g.shape[0], np.uint8)
+    _check(_lib.stq_allocate_bits(int(g.shape[0]), C.c_void_p(g.ctypes.data), C.c_void_p(m.ctypes.data),
+                                  float(avg_bits), int(n_pivots), C.c_void_p(out.ctypes.data)),
+           "stq_allocate_bits")
+    return out

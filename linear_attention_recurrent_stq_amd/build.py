@@ -8,7 +8,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libstq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("stq_host.cpp", "stq_kernels.hip", "stq_window.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f)
+           for f in ("stq_host.cpp", "stq_alloc.cpp", "stq_kernels.hip", "stq_window.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -130,6 +130,11 @@ stq_status check_batch(const stq_pool *pool, int32_t B, const int32_t *ids) {
 
 }  // namespace
 
+namespace stq {
+// The last-error text of this thread, for the other host sources.
+void set_error(const std::string &msg) { g_err = msg; }
+}  // namespace stq
+
 extern "C" {
 
 const char *stq_status_string(stq_status s) {
