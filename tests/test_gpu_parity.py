@@ -80,6 +80,23 @@ def test_mixed_row_widths_d64():
     _run(w, 20, bits=bits, check_slots_every=5, tag="kda-mixed")
 
 
+def test_allocated_row_widths_d128():
+    """KDA key-row widths from stq_allocate_bits (seeded gate means and state
+    magnitudes, mean 6 bits, 1 % pivots): rows of 4, 6, 8 and 16 bits mixed
+    within each d = 128 head; every unit over 12 steps from the outlier
+    start, slot bytes compared every 4 steps."""
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["kimi_kda"].with_(B=6, name="kda_allocated")
+    rng = np.random.default_rng(7)
+    n = w.H * w.dk
+    gate = (0.8 + 0.2 / (1 + np.exp(-rng.normal(2, 1, n)))).astype(np.float32)
+    msq = rng.lognormal(-2.0, 1.5, n).astype(np.float32)
+    bits = stq.allocate_bits(gate, msq, 6.0, n // 100)
+    per_head = bits.reshape(w.H, w.dk)
+    assert sum(len(set(r.tolist())) > 2 for r in per_head) > w.H // 2  # mixed heads
+    _run(w, 12, bits=bits, check_slots_every=4, tag="kda-allocated")
+
+
 def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None, bits=None):
     """Full batch on the GPU; n_units seeded (request, head) units (or the
     given list) followed by the oracle over T steps (the others keep their
