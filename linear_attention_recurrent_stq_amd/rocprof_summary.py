@@ -7,6 +7,10 @@
       each scaled by what the same counter reads for the plain device copy of
       COPY_BYTES bytes (read COPY_BYTES + write COPY_BYTES) in the same run.
 
+  python -m linear_attention_recurrent_stq_amd.rocprof_summary valu DIR WORKLOAD CMD OUT
+      VALU instructions per stq_decode_step call from an SQ_INSTS_VALU /
+      SQ_WAVES pass, and VALU issues per state element (x 64 lanes / elements)
+
 CMD is the command line that produced DIR (recorded in the summary).  The
 decode kernels are k_step (every-step mode) and k_win + k_win_end (windowed:
 one stq_decode_step call launches both).
@@ -111,11 +115,41 @@ def counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, cmd
     print("\n".join(lines))
 
 
+def valu(d: str, workload: str, cmd: str, out: str) -> None:
+    sys.path.insert(0, ROOT)
+    import synth
+    w = synth.WORKLOADS[workload]
+    insts, names, _ = _counter(d, "SQ_INSTS_VALU")
+    waves, _, _ = _counter(d, "SQ_WAVES")
+    if not insts or not waves:
+        raise SystemExit("no decode-kernel dispatch in the counter run")
+    # one stq_decode_step call launches k_win and k_win_end in the windowed mode
+    calls = len(insts) // (2 if w.window > 1 else 1)
+    per_launch = sum(insts) / calls
+    waves_per_launch = sum(waves) / calls
+    elements = w.B * w.H * w.dk * w.dv
+    lines = [f"# rocprofv3 VALU instruction counts per stq_decode_step call, workload {workload}",
+             f"# command: {cmd}",
+             f"workload: {workload}",
+             f"kernels: {', '.join(names)}",
+             f"kernel_source_sha256: {_source_hash()}",
+             f"calls_measured: {calls}",
+             f"sq_insts_valu_per_launch: {per_launch:.0f}",
+             f"sq_waves_per_launch: {waves_per_launch:.0f}",
+             f"valu_insts_per_wave: {per_launch / waves_per_launch:.1f}",
+             f"state_elements_per_launch: {elements}",
+             f"valu_issues_per_element: {per_launch * 64 / elements:.2f}"]
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 if __name__ == "__main__":
     a = sys.argv[1:]
     if a and a[0] == "stats" and len(a) == 5:
         stats(a[1], a[2], a[3], a[4])
     elif a and a[0] == "counters" and len(a) == 7:
         counters(a[1], a[2], a[3], int(a[4]), a[5], a[6])
+    elif a and a[0] == "valu" and len(a) == 5:
+        valu(a[1], a[2], a[3], a[4])
     else:
         raise SystemExit(__doc__)
