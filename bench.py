@@ -8,10 +8,18 @@ stq_decode_step launches, each reading and rewriting every state of its layer.
 Inputs are resident in HBM before timing (a ring of 16 pre-generated steps,
 shared by the layers: values do not change the cost).
 
+Protocol: W warm-up steps, continued until at least --warmup-seconds of
+warm-up have run (clocks and caches settle; the JSON records how many warm-up
+steps ran), then exactly K timed steps between two HIP events on the launch
+stream, with a device synchronization on both sides and no other event inside.
+A second, untimed pass then records events around each launch to give the
+launch-time distribution.
+
 Prints one JSON line: head-updates/s (value), tokens/s, algorithmic HBM GB/s
-and its fraction of the 8 TB/s peak for the step kernel (per-launch HIP events
-on the launch stream), and the CPU oracle's throughput on a bounded sample of
-the same workload (cpu_baseline).
+and its fraction of the 8 TB/s peak for the step kernel (algorithmic bytes per
+launch over the timed region's time per launch), and the CPU oracle's
+throughput on a bounded sample of the same workload (cpu_baseline, on all
+usable host threads up to 16 and on one thread).
 """
 from __future__ import annotations
 
@@ -77,11 +85,17 @@ def launch_bytes(w: synth.Workload, bits: np.ndarray) -> float:
     return w.B * (state + state / W + w.H * per_head / W + io)
 
 
+# the sources the device code is compiled from (host-only files excluded)
+DEVICE_SOURCES = ("stq_device.h", "stq_internal.h", "stq_kernels.hip", "stq_window.hip")
+
+
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrent_stq_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f not in DEVICE_SOURCES and not f.endswith(".hip"):
+            continue
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -104,33 +118,45 @@ def counter_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
+def _oracle_rate(w: synth.Workload, units: int, steps: int, threads: int, seed: int):
     """The oracle, as it stands, on `units` seeded (request, head) states of the
-    workload for `steps` steps, one oracle call per state-step, spread over
-    host threads (the oracle itself is single-threaded per call)."""
+    workload for `steps` steps, one oracle call per state-step, over `threads`
+    host threads (the oracle itself is single-threaded per call).  Returns
+    (head-updates/s, seconds)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
     bits = synth.unit_bits(w)
     cfg = oracle.Cfg.from_workload(w, bits)
-    rng = np.random.default_rng(7)
+    rng = np.random.default_rng(seed)
     ub = rng.integers(0, w.B, units)
     uh = rng.integers(0, w.H, units)
     xs = [synth.step_inputs(w, 0, t, ub, uh) for t in range(steps)]
     slots = [cfg.new_slot() for _ in range(units)]
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    gate_vec = w.gate == "keyvec"
 
     def run(n):
         for t in range(steps):
             x = xs[t]
-            cfg.step_head(slots[n], int(uh[n]), x.q[n], x.k[n], x.v[n],
-                          x.a[n] if gate_vec else x.a[n], x.beta[n])
+            cfg.step_head(slots[n], int(uh[n]), x.q[n], x.k[n], x.v[n], x.a[n], x.beta[n])
 
     t0 = time.perf_counter()
-    with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(run, range(units)))
+    if threads == 1:
+        for n in range(units):
+            run(n)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, range(units)))
     dt = time.perf_counter() - t0
+    return units * steps / dt, dt
+
+
+def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
+    """The oracle on this host: all usable threads (at most 16) over disjoint
+    states, and one thread on a smaller sample (head-updates/s per core)."""
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    rate, dt = _oracle_rate(w, units, steps, threads, 7)
+    u1, s1 = 64, 64
+    rate1, dt1 = _oracle_rate(w, u1, s1, 1, 8)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -139,9 +165,12 @@ def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
                 break
     except OSError:
         pass
-    return {"value": units * steps / dt, "unit": "head-updates/s", "cores": threads, "kind": "oracle",
+    return {"value": round(rate, 1), "unit": "head-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"{units} seeded (request, head) states x {steps} steps of {w.name} layer 0 "
-                      f"({units * steps} head-updates, {dt:.2f} s wall on {threads} threads, {cpu})"}
+                      f"({units * steps} head-updates, {dt:.2f} s wall on {threads} threads, {cpu})",
+            "single_thread": {"value": round(rate1, 1), "unit": "head-updates/s", "cores": 1,
+                              "sample": f"{u1} states x {s1} steps ({u1 * s1} head-updates, "
+                                        f"{dt1:.2f} s on one thread)"}}
 
 
 def main() -> int:
@@ -149,6 +178,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (whole steps) until this much time has passed")
+    ap.add_argument("--launch-pass", type=int, default=64,
+                    help="steps of the untimed pass with events around each launch")
     ap.add_argument("--workload", default="serving_gdn", choices=list(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=512)
@@ -193,18 +226,27 @@ def main() -> int:
             stq.pack(pool, ids, torch.from_numpy(synth.initial_state(w, l, bb, hh)).to(dev))
     torch.cuda.synchronize()
 
+    stream = torch.cuda.current_stream()
+
     def one_step(t, evs=None):
         r = t % RING
         for l, (L, pool, _) in enumerate(layers):
             if evs is not None:
-                evs[l][0].record()
-            stq.decode_step(pool, ids, qs[r], ks[r], vs[r], as_[r], bs[r], o)
+                evs[l][0].record(stream)
+            stq.decode_step(pool, ids, qs[r], ks[r], vs[r], as_[r], bs[r], o, stream=stream)
             if evs is not None:
-                evs[l][1].record()
+                evs[l][1].record(stream)
 
-    for t in range(args.warmup):
-        one_step(t)
+    # warm-up: W steps, then whole steps until the time budget has passed
+    t0 = time.perf_counter()
+    nwarm = 0
+    while nwarm < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
+        one_step(nwarm)
+        nwarm += 1
+        if nwarm % 64 == 0 or nwarm == args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t0
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -214,27 +256,33 @@ def main() -> int:
         del src, dst
 
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(w.layers)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
+    t_start.record(stream)
     for t in range(K):
-        one_step(args.warmup + t, ev[t])
+        one_step(nwarm + t)
         if (t + 1) % 512 == 0:
             print(f"# timed step {t + 1}/{K}", file=sys.stderr, flush=True)
-    t_end.record()
+    t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+
+    # untimed pass: events around every launch (the kernel-time distribution)
+    NP = max(1, args.launch_pass)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.layers)] for _ in range(NP)]
+    for t in range(NP):
+        one_step(nwarm + K + t, ev[t])
+    torch.cuda.synchronize()
     launch_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
 
     head_updates = w.B * w.H * w.layers * K
     value = head_updates / (total_ms * 1e-3)
     per_launch_bytes = np.mean([launch_bytes(w, bits) for (_, _, bits) in layers])
-    avg_launch_s = float(launch_ms.mean()) * 1e-3
+    avg_launch_s = total_ms * 1e-3 / (K * w.layers)
     achieved = per_launch_bytes / avg_launch_s / 1e9
     rec = {
         "metric": METRIC,
@@ -243,6 +291,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_run": {"steps": nwarm, "seconds": round(warm_s, 3)},
         "ms_per_step": round(total_ms / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -258,7 +307,9 @@ def main() -> int:
         "tokens_per_s": round(w.B * K / (total_ms * 1e-3), 1),
         "hbm_gbs": round(achieved, 1),
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-        "launch_us": {"mean": round(float(launch_ms.mean()) * 1e3, 2),
+        "launch_us": {"timed_region_mean": round(avg_launch_s * 1e6, 2),
+                      "events_pass_steps": NP,
+                      "mean": round(float(launch_ms.mean()) * 1e3, 2),
                       "p10": round(float(np.percentile(launch_ms, 10)) * 1e3, 2),
                       "p50": round(float(np.percentile(launch_ms, 50)) * 1e3, 2),
                       "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},

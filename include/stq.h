@@ -17,7 +17,9 @@
  *    rejected call writes nothing, on the host or the device.
  *  - No call synchronizes the device; work is queued on `stream` (a
  *    hipStream_t; NULL is the default stream).  Launch failures return
- *    STQ_ERR_DEVICE with the HIP error text in stq_last_error().
+ *    STQ_ERR_DEVICE with the HIP error text in stq_last_error().  (A library
+ *    built with STQ_DEBUG_VALIDATE copies slot ids back to the host to check
+ *    them, which synchronizes; see stq_check_slot_ids.)
  *  - Device memory is always the caller's; the library never allocates it.
  *    Device pointers must be 16-byte aligned (slot ids: 4-byte).
  *  - A pool must not be used by two calls that overlap in time (e.g. on two
@@ -136,6 +138,16 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
  * Current state of B slots as fp32 [B,H,d_k,d_v] (key-row-major): the
  * dequantized codes (n * r * c, FP16 pivots as stored; windowed: the base with
  * its compensation entries, materialized with the stored deltas and gate).
+ * This is the "unpack" stage of the fused decode kernel (STEPQuant essay,
+ * experiment-design paragraph: the state is unpacked, updated and written out
+ * in one kernel) offered on its own; for the windowed mode it is the
+ * materialization of the fixed low-bit base, the fp32 window updates and the
+ * compensation entries (LeapQuant article, "研究の概要").
+ *   d_slot_ids [B] int32  device, distinct, in [0, slots); an id out of range
+ *                         gives NaN for that request's states
+ *   d_state    [B,H,d_k,d_v] fp32 device output, 16-byte aligned
+ * Errors: STQ_ERR_INVALID (NULL pool/ids/state, B < 0 or B > slots),
+ * STQ_ERR_ALIGN, STQ_ERR_DEVICE; nothing is written then.
  */
 stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
                       float *d_state, void *stream);
@@ -144,9 +156,33 @@ stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids
  * Quantize fp32 states [B,H,d_k,d_v] into B slots (column then row absmax
  * scales, codes, FP16 pivots; windowed: top-K compensation entries, gate 1,
  * no deltas).  Used to seed initial states and to inspect requantization.
+ * This is the "write out" stage of the fused decode kernel with its scale
+ * fitting and compressed store (STEPQuant essay, experiment-design paragraph:
+ * the dual-axis scales are refitted to the state being stored); for the
+ * windowed mode it is the requantization at a window end, with the largest
+ * entries kept at high precision (LeapQuant article, "研究の概要").
+ *   d_slot_ids [B] int32  device, distinct, in [0, slots); an id out of range
+ *                         is skipped (nothing written for that request)
+ *   d_state    [B,H,d_k,d_v] fp32 device input, 16-byte aligned, not modified
+ * Errors: as stq_unpack.
  */
 stq_status stq_pack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
                     const float *d_state, void *stream);
+
+/*
+ * Host check of a batch's slot ids: every id in [0, pool->slots) and no id
+ * twice.  Two requests of one call on the same slot would make two workgroups
+ * read-modify-write one state with no ordering between them, so the calls
+ * require distinct ids (the serving pool keeps one reserved slot per live
+ * request: STEPQuant essay, opening paragraphs).  The release library does
+ * not copy device ids back to check them on every call (that would
+ * synchronize the stream); a library built with STQ_DEBUG_VALIDATE does, and
+ * then rejects a bad batch in stq_decode_step, stq_unpack and stq_pack before
+ * anything is launched.
+ *   h_slot_ids [B] int32 host
+ * Returns STQ_OK, or STQ_ERR_INVALID naming the first bad position.
+ */
+stq_status stq_check_slot_ids(const stq_pool *pool, int32_t B, const int32_t *h_slot_ids);
 
 /*
  * Lifetime-aware bit allocation (host only; STEPQuant essay, temporal-axis

@@ -32,7 +32,7 @@ NONE, F32, F16, BF16 = 0, 1, 2, 3
 
 SYMBOLS = ["stq_status_string", "stq_last_error", "stq_pack_layout", "stq_layout_query",
            "stq_layout_head", "stq_layout_free", "stq_alloc_pool", "stq_decode_step",
-           "stq_unpack", "stq_pack", "stq_allocate_bits"]
+           "stq_unpack", "stq_pack", "stq_check_slot_ids", "stq_allocate_bits"]
 
 
 class StqConfig(C.Structure):
@@ -62,8 +62,9 @@ _lib.stq_decode_step.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P, _P, 
 _lib.stq_unpack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
 _lib.stq_pack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
 _lib.stq_allocate_bits.argtypes = [C.c_int32, _P, _P, C.c_double, C.c_int32, _P]
+_lib.stq_check_slot_ids.argtypes = [C.POINTER(StqPool), C.c_int32, _P]
 for _f in ("stq_pack_layout", "stq_layout_query", "stq_layout_head", "stq_alloc_pool",
-           "stq_decode_step", "stq_unpack", "stq_pack", "stq_allocate_bits"):
+           "stq_decode_step", "stq_unpack", "stq_pack", "stq_check_slot_ids", "stq_allocate_bits"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -207,6 +208,15 @@ def pack(pool: Pool, slot_ids, state, stream=None) -> None:
         raise ValueError("state must be [B,H,d_k,d_v]")
     _check(_lib.stq_pack(C.byref(pool.pool), B, _dptr(slot_ids, "slot_ids", torch.int32),
                          _dptr(state, "state", torch.float32), _stream_ptr(stream)), "stq_pack")
+
+
+def check_slot_ids(pool: "Pool", slot_ids) -> None:
+    """stq_check_slot_ids on host ids (numpy, list, or a tensor copied to the
+    host): raises StqError naming the first out-of-range or repeated id."""
+    ids = np.ascontiguousarray(
+        slot_ids.cpu().numpy() if hasattr(slot_ids, "cpu") else slot_ids, dtype=np.int32)
+    _check(_lib.stq_check_slot_ids(C.byref(pool.pool), int(ids.size), C.c_void_p(ids.ctypes.data)),
+           "stq_check_slot_ids")
 
 
 def allocate_bits(gate_mean, state_msq, avg_bits: float, n_pivots: int):

@@ -1,9 +1,9 @@
 """Build the HIP library in-tree: ``libstq.so`` next to this file (gfx950 only).
 
 Each source is compiled to an object of its own (in parallel, under
-``_build/``) and the objects are linked into the shared library.  With
-``debug_validate=True`` the same sources are built with STQ_DEBUG_VALIDATE
-into ``libstq_debug.so``: every call that takes slot ids then copies them to
+``_build/``) and the objects are linked into the shared library.  The same
+kernels are also linked with the host source built with STQ_DEBUG_VALIDATE
+into ``libstq_debug.so``: there every call that takes slot ids copies them to
 the host and rejects duplicates and out-of-range ids before any launch.
 """
 from __future__ import annotations
@@ -41,37 +41,42 @@ def _jobs() -> int:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n, len(SOURCES)))
+    return max(1, min(16, n, len(SOURCES) + 1))
 
 
-def build(verbose: bool = False, debug_validate: bool = False) -> str:
-    """Compile every source and link the library (always recompiles)."""
-    tag = "debug" if debug_validate else "release"
-    objdir = os.path.join(OBJDIR, tag)
-    os.makedirs(objdir, exist_ok=True)
-    extra = ["-DSTQ_DEBUG_VALIDATE=1"] if debug_validate else []
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libstq.so and libstq_debug.so (always
+    recompiles).  Returns the path of libstq.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
+    host = SOURCES[0]
+    jobs = [(src, os.path.join(OBJDIR, os.path.basename(src) + ".o"), []) for src in SOURCES]
+    jobs.append((host, os.path.join(OBJDIR, "debug_" + os.path.basename(host) + ".o"),
+                 ["-DSTQ_DEBUG_VALIDATE=1"]))
 
-    def compile_one(src: str) -> str:
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    def compile_one(job):
+        src, obj, extra = job
         cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
         return obj
 
+    # the largest source first, so the others compile beside it
+    order = sorted(jobs, key=lambda j: -os.path.getsize(j[0]))
     with ThreadPoolExecutor(_jobs()) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    out = LIB_DEBUG if debug_validate else LIB
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, out)
-    return out
+        list(ex.map(compile_one, order))
+    objs = [j[1] for j in jobs]
+    for out, use in ((LIB, objs[:len(SOURCES)]), (LIB_DEBUG, [objs[-1]] + objs[1:len(SOURCES)])):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *use, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return LIB
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv, debug_validate="--debug-validate" in sys.argv)
-    print(LIB_DEBUG if "--debug-validate" in sys.argv else LIB)
+    build(verbose="-v" in sys.argv)
+    print(LIB, LIB_DEBUG)

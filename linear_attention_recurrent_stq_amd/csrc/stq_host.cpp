@@ -119,12 +119,41 @@ stq_status launched(hipError_t e, const char *what) {
     return STQ_OK;
 }
 
+// Every id in [0, slots), none twice (host ids).
+stq_status check_ids_host(int32_t slots, int32_t B, const int32_t *ids) {
+    std::vector<uint8_t> seen((size_t)slots, 0);
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t s = ids[b];
+        char m[128];
+        if (s < 0 || s >= slots) {
+            std::snprintf(m, sizeof m, "slot id %d at position %d is outside [0, %d)", s, b, slots);
+            return fail(STQ_ERR_INVALID, m);
+        }
+        if (seen[(size_t)s]) {
+            std::snprintf(m, sizeof m, "slot id %d at position %d appears twice in the batch", s, b);
+            return fail(STQ_ERR_INVALID, m);
+        }
+        seen[(size_t)s] = 1;
+    }
+    return STQ_OK;
+}
+
 stq_status check_batch(const stq_pool *pool, int32_t B, const int32_t *ids) {
     if (stq_status s = check_pool(pool)) return s;
     if (B < 0) return fail(STQ_ERR_INVALID, "B must be >= 0");
     if (B > pool->slots) return fail(STQ_ERR_INVALID, "B exceeds the pool's slot count");
     if (B > 0 && !ids) return fail(STQ_ERR_INVALID, "slot ids are NULL");
     if (B > 0 && !aligned(ids, 4)) return fail(STQ_ERR_ALIGN, "slot ids must be 4-byte aligned");
+#if STQ_DEBUG_VALIDATE
+    // debug builds: copy the ids back (a synchronizing copy) and check them
+    if (B > 0) {
+        std::vector<int32_t> h((size_t)B);
+        const hipError_t e = hipMemcpy(h.data(), ids, sizeof(int32_t) * (size_t)B, hipMemcpyDeviceToHost);
+        if (e != hipSuccess)
+            return fail(STQ_ERR_DEVICE, std::string("slot id copy: ") + hipGetErrorString(e));
+        if (stq_status s = check_ids_host(pool->slots, B, h.data())) return s;
+    }
+#endif
     return STQ_OK;
 }
 
@@ -150,6 +179,14 @@ const char *stq_status_string(stq_status s) {
 }
 
 const char *stq_last_error(void) { return g_err.c_str(); }
+
+stq_status stq_check_slot_ids(const stq_pool *pool, int32_t B, const int32_t *h_slot_ids) {
+    g_err.clear();
+    if (!pool || !pool->layout) return fail(STQ_ERR_INVALID, "pool is NULL");
+    if (B < 0 || B > pool->slots) return fail(STQ_ERR_INVALID, "B must be in [0, slots]");
+    if (B > 0 && !h_slot_ids) return fail(STQ_ERR_INVALID, "slot ids are NULL");
+    return check_ids_host(pool->slots, B, h_slot_ids);
+}
 
 stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
     g_err.clear();

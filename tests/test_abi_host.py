@@ -162,3 +162,46 @@ def test_calls_validate_before_launch(stq):
     assert lib.stq_alloc_pool(L.handle, 4, P(0x100000), 100, None, C.byref(out)) == stq.STQ_ERR_TOO_SMALL
     assert lib.stq_alloc_pool(L.handle, 4, P(0x100008), 1 << 20, None, C.byref(out)) == stq.STQ_ERR_ALIGN
     assert lib.stq_layout_head(L.handle, 7, C.byref(small), None) == stq.STQ_ERR_INVALID
+
+
+def test_check_slot_ids_on_host(stq):
+    """stq_check_slot_ids: distinct ids in range pass; a repeated id, a
+    negative id and an id past the slot count are rejected, naming the
+    first bad position."""
+    w = synth.WORKLOADS["qwen_gdn"]
+    L = stq.Layout.from_workload(w, synth.unit_bits(w))
+    pool = stq.StqPool(None, 0, 8, L.handle)
+    lib = stq.library()
+
+    def check(ids):
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        return lib.stq_check_slot_ids(C.byref(pool), a.size, C.c_void_p(a.ctypes.data))
+
+    assert check([3, 0, 7, 1]) == stq.STQ_OK
+    assert check(np.arange(8)[::-1]) == stq.STQ_OK
+    assert check([]) == stq.STQ_OK
+    assert check([2, 5, 2]) == stq.STQ_ERR_INVALID
+    assert b"position 2" in lib.stq_last_error() and b"twice" in lib.stq_last_error()
+    assert check([1, -1]) == stq.STQ_ERR_INVALID
+    assert b"position 1" in lib.stq_last_error()
+    assert check([0, 8]) == stq.STQ_ERR_INVALID
+    assert b"outside [0, 8)" in lib.stq_last_error()
+    # more ids than slots is a bad batch before any id is read
+    assert lib.stq_check_slot_ids(C.byref(pool), 9, None) == stq.STQ_ERR_INVALID
+    # the binding raises with the library's text
+    with pytest.raises(stq.StqError, match="twice"):
+        class _P:  # a pool-like object over the same view
+            pass
+        p = _P()
+        p.pool = pool
+        stq.check_slot_ids(p, [4, 4])
+
+
+def test_debug_validate_library_loads_and_exports(stq):
+    """The STQ_DEBUG_VALIDATE build (the same kernels, a host side that
+    checks slot ids before every launch) loads and exports every declared
+    function."""
+    path = os.path.join(ROOT, "linear_attention_recurrent_stq_amd", "libstq_debug.so")
+    lib = C.CDLL(path)
+    for name in stq.SYMBOLS:
+        assert hasattr(lib, name), name

@@ -467,3 +467,57 @@ def test_windowed_sampled_units_all_1024_steps():
     """Full windowed batch, 256 followed units over all 1024 steps (64 window ends)."""
     w = synth.WORKLOADS["windowed_kda"]
     _run_sampled(w, w.T, 256, seed=13, tag="win-long")
+
+
+def test_debug_validate_build_rejects_bad_batches():
+    """The STQ_DEBUG_VALIDATE library checks the device slot ids on the host
+    before launching: a batch with a repeated id or an id out of range is
+    rejected with STQ_ERR_INVALID and the pool is left as it was; a good batch
+    steps exactly like the release library."""
+    import ctypes as C
+    import os
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    path = os.path.join(os.path.dirname(stq.__file__), "libstq_debug.so")
+    dbg = C.CDLL(path)
+    P = C.c_void_p
+    dbg.stq_pack_layout.argtypes = [C.POINTER(stq.StqConfig), C.POINTER(P)]
+    dbg.stq_alloc_pool.argtypes = [P, C.c_int32, P, C.c_size_t, P, C.POINTER(stq.StqPool)]
+    dbg.stq_decode_step.argtypes = [C.POINTER(stq.StqPool), C.c_int32, P, P, P, P, P, P, P, P]
+    dbg.stq_last_error.restype = C.c_char_p
+    dbg.stq_layout_free.argtypes = [P]
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=6)
+    hs = _harness(w)
+    try:
+        x = hs.load_full(0)
+        cfg = hs.L.cfg
+        h = P()
+        assert dbg.stq_pack_layout(C.byref(cfg), C.byref(h)) == stq.STQ_OK
+        q = stq.StqPool()
+        assert dbg.stq_alloc_pool(h, w.B, None, 0, None, C.byref(q)) == stq.STQ_OK
+        buf = torch.empty(q.bytes, dtype=torch.uint8, device="cuda")
+        pool = stq.StqPool()
+        s = P(torch.cuda.current_stream().cuda_stream)
+        assert dbg.stq_alloc_pool(h, w.B, P(buf.data_ptr()), q.bytes, s, C.byref(pool)) == stq.STQ_OK
+        ptr = lambda t: P(t.data_ptr())
+
+        def step(ids):
+            return dbg.stq_decode_step(C.byref(pool), w.B, ptr(ids), ptr(hs.q), ptr(hs.k), ptr(hs.v),
+                                       ptr(hs.a), ptr(hs.beta), ptr(hs.o), s)
+
+        torch.cuda.synchronize()
+        before = buf.cpu()
+        for bad in ([0, 1, 2, 3, 1, 5], [0, 1, 2, 3, 4, 6], [0, -1, 2, 3, 4, 5]):
+            ids = torch.tensor(bad, dtype=torch.int32, device="cuda")
+            assert step(ids) == stq.STQ_ERR_INVALID, bad
+            print(f"[debug-validate] {bad}: {dbg.stq_last_error().decode()}", flush=True)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.cpu(), before)
+        assert step(hs.slot_ids) == stq.STQ_OK
+        hs.step(x)  # the release library on the harness's own pool
+        torch.cuda.synchronize()
+        hdr = hs.L.header_bytes
+        assert torch.equal(buf[hdr:].cpu(), hs.pool.buffer[hdr:].cpu())
+        dbg.stq_layout_free(h)
+    finally:
+        hs.close()
