@@ -41,25 +41,34 @@
  *              qmax = 2^(b-1)-1; row i is a little-endian LSB-first bit
  *              stream, code j at bits [j*b, (j+1)*b).
  *
- * Per-step mode (window == 1), one state:
- *   decay+dequant  g_i = RN(a_i*r_i);  A_ij = RN(RN(n_ij*g_i)*c_j)
- *                  (no column scale: A_ij = RN(n_ij*g_i));
- *                  pivot row: A_ij = RN(a_i*h_ij); fp32 row: A_ij = RN(a_i*m_ij)
- *   read           w_j = csum(A_.j, k)
- *   delta          u_j = RN(beta*RN(v_j - w_j))
- *   write          M_ij = fma(k_i, u_j, A_ij)
- *   output         o_j = csum(M_.j, q)
- *   column scale   C_j = max over non-pivot rows |M_ij|; c'_j = H(C_j);
- *                  ic_j = c'_j > 0 ? RN(1/c'_j) : 0;  Z_ij = RN(M_ij*ic_j)
- *                  (no column scale: Z = M)
+ * Per-step mode (window == 1), one state.  The stored state is the product
+ * diag(r) N diag(c) of the dual-axis fit; the step keeps it in that factored
+ * form: the row factor (with the gate) scales the codes, and the column
+ * factor s_j multiplies each column once, on the value side (w, o, u),
+ * instead of every entry.  The working state M''_ij = M_ij / s_j is the
+ * state in units of the stored column scale.
+ *   column factor  s_j = c_j if column scales are on and c_j > 0, else 1;
+ *                  is_j = RN(1/s_j)
+ *   decay+dequant  g_i = RN(a_i*r_i);  A_ij = RN(n_ij*g_i)
+ *                  pivot row: A_ij = RN(RN(a_i*h_ij)*is_j);
+ *                  fp32 row: A_ij = RN(a_i*m_ij) (fp32 heads have s = 1)
+ *   read           w_j = RN(s_j*csum(A_.j, k))
+ *   delta          u_j = RN(beta*RN(v_j - w_j));  u'_j = RN(u_j*is_j)
+ *   write          M''_ij = fma(k_i, u'_j, A_ij)
+ *   output         o_j = RN(s_j*csum(M''_.j, q))
+ *   column scale   C_j = max over non-pivot rows |M''_ij|; c'_j = H(RN(C_j*s_j));
+ *                  f_j = c'_j > 0 ? RN(s_j/c'_j) : 0;  Z_ij = RN(M''_ij*f_j)
+ *                  (no column scale: Z = M'')
  *   row scale      R_i = max_j |Z_ij|;  r'_i = Hup(RN(R_i/qmax_i))  (fp32 row
  *                  scale: r'_i = RN(R_i/qmax_i));  ir_i = RN(1/r'_i), or 0 when
  *                  r'_i = 0 or 1/r'_i overflows.  Rounding the step up means
  *                  |Z_ij*ir_i| < qmax + 1/2, so the clamp below only acts when
  *                  the step saturated at 65504.
  *   codes          n'_ij = clamp(rne(Z_ij*ir_i exactly), -qmax_i, qmax_i)
- *                  pivot row: h'_ij = H(M_ij); fp32 row: m'_ij = M_ij
+ *                  pivot row: h'_ij = H(RN(M''_ij*s_j)); fp32 row: m'_ij = M''_ij
  *                  (pivot and fp32 rows are left out of both scale maxima)
+ * Requantizing an fp32 state M directly (pack, window end) is the same with
+ * s = 1: c'_j = H(C_j), f_j = RN(1/c'_j).
  *
  * Windowed mode (window W > 1), base B_ij = RN(n_ij*r_i*c_j) (pivot: h_ij;
  * compensation positions: their fp32 value), cumulative gate g (1 at a
@@ -400,13 +409,17 @@ static void dequant_base(const ora_cfg *c, const ora_unit *u, float *B, int with
         }
 }
 
-/* Requantize M into u (codes, pivots, scales).  skip[e] != 0 excludes an entry. */
-static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint8_t *skip) {
+/* Requantize into u (codes, pivots, scales) the state whose column j is
+ * M[., j] * s[j] (s == NULL: all ones, M is the state itself).  skip[e] != 0
+ * excludes an entry. */
+static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const float *s,
+                       const uint8_t *skip) {
     int dk = c->dk, dv = c->dv;
-    float *ic = malloc(sizeof(float) * (size_t)dv);
+    float *f = malloc(sizeof(float) * (size_t)dv);
     float *Z = malloc(sizeof(float) * (size_t)dk * dv);
     for (int j = 0; j < dv; ++j) {
-        if (!c->cscale_f16) { u->c[j] = 1.0f; ic[j] = 1.0f; continue; }
+        if (!c->cscale_f16) { u->c[j] = 1.0f; f[j] = 1.0f; continue; }
+        float sj = s ? s[j] : 1.0f;
         float C = 0.0f;
         for (int i = 0; i < dk; ++i) {
             size_t e = (size_t)i * dv + j;
@@ -414,8 +427,8 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
             float a = fabsf(M[e]);
             if (a > C) C = a;
         }
-        u->c[j] = f16_val(H(C));
-        ic[j] = u->c[j] > 0.0f ? 1.0f / u->c[j] : 0.0f;
+        u->c[j] = f16_val(H(C * sj));
+        f[j] = u->c[j] > 0.0f ? sj / u->c[j] : 0.0f;
     }
     for (int i = 0; i < dk; ++i) {
         if (u->bw[i] >= 16) {
@@ -423,8 +436,9 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
             u->r[i] = 0.0f;
             for (int j = 0; j < dv; ++j) {
                 size_t e = (size_t)i * dv + j;
-                if (u->bw[i] == 32) u->fv[e] = M[e];
-                else u->hv[e] = H(M[e]);
+                float sj = s ? s[j] : 1.0f;
+                if (u->bw[i] == 32) u->fv[e] = M[e] * sj;
+                else u->hv[e] = H(M[e] * sj);
                 u->n[e] = 0;
             }
             continue;
@@ -432,7 +446,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
         float R = 0.0f;
         for (int j = 0; j < dv; ++j) {
             size_t e = (size_t)i * dv + j;
-            Z[e] = (skip && skip[e]) ? 0.0f : (c->cscale_f16 ? M[e] * ic[j] : M[e]);
+            Z[e] = (skip && skip[e]) ? 0.0f : (c->cscale_f16 ? M[e] * f[j] : M[e]);
             float a = fabsf(Z[e]);
             if (a > R) R = a;
         }
@@ -451,7 +465,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const uint
             u->hv[e] = 0;
         }
     }
-    free(ic);
+    free(f);
     free(Z);
 }
 
@@ -538,7 +552,7 @@ void ora_pack_head(const ora_cfg *c, int h, uint8_t *slot, const float *M) {
         memset(u.du, 0, sizeof(float) * (size_t)c->window * c->dv);
         memset(u.dkap, 0, sizeof(float) * (size_t)c->window * c->dk);
     }
-    requantize(c, &u, M, skip);
+    requantize(c, &u, M, NULL, skip);
     unit_write(c, h, slot, &u);
     free(skip);
     unit_free(&u);
@@ -559,27 +573,36 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
 
     if (c->window == 1) {
         float *A = malloc(sizeof(float) * e);
+        float *sc = malloc(sizeof(float) * (size_t)dv);
+        float *is = malloc(sizeof(float) * (size_t)dv);
+        /* u.c is 1 where the head has no column scales */
+        for (int j = 0; j < dv; ++j) {
+            sc[j] = u.c[j] > 0.0f ? u.c[j] : 1.0f;
+            is[j] = 1.0f / sc[j];
+        }
         for (int i = 0; i < dk; ++i) {
             float gi = ai[i] * u.r[i];
             for (int j = 0; j < dv; ++j) {
                 size_t x = (size_t)i * dv + j;
                 if (u.bw[i] == 32) A[x] = ai[i] * u.fv[x];
-                else if (u.bw[i] == 16) A[x] = ai[i] * f16_val(u.hv[x]);
-                else if (c->cscale_f16) A[x] = ((float)u.n[x] * gi) * u.c[j];
+                else if (u.bw[i] == 16) A[x] = (ai[i] * f16_val(u.hv[x])) * is[j];
                 else A[x] = (float)u.n[x] * gi;
             }
         }
         for (int j = 0; j < dv; ++j) {
-            float w = csum(A + j, (size_t)dv, k, dk);
+            float w = sc[j] * csum(A + j, (size_t)dv, k, dk);
             float uj = beta * (v[j] - w);
+            float us = uj * is[j];
             for (int i = 0; i < dk; ++i) {
                 size_t x = (size_t)i * dv + j;
-                M[x] = fmaf(k[i], uj, A[x]);
+                M[x] = fmaf(k[i], us, A[x]);
             }
         }
-        for (int j = 0; j < dv; ++j) o[j] = csum(M + j, (size_t)dv, q, dk);
-        requantize(c, &u, M, NULL);
+        for (int j = 0; j < dv; ++j) o[j] = sc[j] * csum(M + j, (size_t)dv, q, dk);
+        requantize(c, &u, M, sc, NULL);
         free(A);
+        free(sc);
+        free(is);
     } else {
         int W = c->window, n = u.nd;
         float *B = malloc(sizeof(float) * e);
@@ -629,7 +652,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
                 }
             uint8_t *skip = calloc(e, 1);
             select_comps(c, &u, M, skip);
-            requantize(c, &u, M, skip);
+            requantize(c, &u, M, NULL, skip);
             for (int i = 0; i < dk; ++i) u.g[i] = 1.0f;
             u.nd = 0;   /* the stored deltas are left as they are: only n counts */
             free(skip);
