@@ -15,14 +15,20 @@
 //
 // Arithmetic, per state (every rounding fixed so results are reproducible; the
 // pages state the method in words only: STEPQuant essay, background,
-// temporal-axis, spatial-axis and experiment-design paragraphs):
-//   g_i = RN(a_i r_i);  A_ij = RN(RN(n_ij g_i) c_j)  (pivot row: RN(a_i h_ij))
-//   w_j = csum_i(A_ij k_i);  u_j = RN(beta RN(v_j - w_j))
-//   M_ij = fma(k_i, u_j, A_ij);  o_j = csum_i(M_ij q_i)
-//   c'_j = H(max_i |M_ij|);  Z_ij = RN(M_ij RN(1/c'_j))
+// temporal-axis, spatial-axis and experiment-design paragraphs).  The stored
+// state is diag(r) N diag(c); the step keeps that factored form, so the
+// column scale multiplies each column once on the value side and the working
+// state M'' = M / s is in units of the stored column scale:
+//   s_j = c_j (1 with no column scales or c_j = 0);  is_j = RN(1/s_j)
+//   g_i = RN(a_i r_i);  A_ij = RN(n_ij g_i)  (pivot row: RN(RN(a_i h_ij) is_j))
+//   w_j = RN(s_j csum_i(A_ij k_i));  u_j = RN(beta RN(v_j - w_j));  u'_j = RN(u_j is_j)
+//   M''_ij = fma(k_i, u'_j, A_ij);  o_j = RN(s_j csum_i(M''_ij q_i))
+//   c'_j = H(RN(max_i |M''_ij| s_j));  Z_ij = RN(M''_ij RN(s_j / c'_j))
 //   r'_i = Hup(RN(max_j |Z_ij| / qmax_i)) (smallest fp16 not below; fp32 row
 //   scales: RN);  n'_ij = rne(Z_ij RN(1/r'_i)) -- rounding the step up keeps
-//   |n'| <= qmax, so the clamp is applied only to a row whose step saturated.
+//   |n'| <= qmax, so the clamp is applied only to a row whose step saturated;
+//   pivot rows store H(RN(M''_ij s_j)).  Pack and the window end requantize an
+//   fp32 state directly: the same with s = 1.
 // csum: blocks of 8 rows as fma chains from RN(x0 y0), block sums left to right.
 // Codes are offset binary (u = n + 2^(b-1)) in LSB-first row bit streams.
 #pragma once
@@ -255,9 +261,10 @@ struct Lds {
     float nog[DK];              //   -2^(w-1) g
     float af[DK];               //   gate
     float kf[DK], qf[DK];       //   k and q as fp32
-    float cf[DV];               // column scales (1 when absent)
-    float u[DV];                // u = beta (v - w)
-    float ic[DV];               // 1 / c'
+    float cf[DV];               // column factor s (the column scale, or 1)
+    float isf[DV];              // RN(1 / s)
+    float u[DV];                // u' = RN(beta (v - w) / s)
+    float ic[DV];               // RN(s / c') (pack: RN(1 / c'))
     float ir[DK];               // 1 / r'; negated when the row step saturated
 };
 
@@ -386,6 +393,17 @@ __device__ __forceinline__ uint4 pivot_piece(const float (&x)[8]) {
     return p;
 }
 
+// A pivot row piece of the working state (SCALED: in units of the column
+// factor s): the fp16 of RN(x s).
+template <bool SCALED>
+__device__ __forceinline__ uint4 pivot_piece_s(const float (&x)[8], const float (&s)[8]) {
+    if (!SCALED) return pivot_piece(x);
+    float y[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) y[c] = x[c] * s[c];
+    return pivot_piece(y);
+}
+
 // Quantize one row of 8 values with 1/r' = ir and store the piece.
 template <bool CLAMP>
 __device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir, const float (&x)[8]) {
@@ -401,10 +419,12 @@ __device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir,
 }
 
 // Column scales, row scales, codes and pivots of x (the thread's 8x8 block of
-// the fp32 state) written back into the head region R.  If emit_o, the column
-// partial sums of o are already in sm.colp and o is combined and stored in the
-// same LDS round as the column maxima.
-template <int DK, int DV, int W>
+// the fp32 state) written back into the head region R.  SCALED: x is in units
+// of the column factor s in sm.cf (the step's working state); otherwise x is
+// the state itself (pack, window end).  If emit_o, the column partial sums of
+// o are already in sm.colp and o is combined and stored in the same LDS round
+// as the column maxima.
+template <int DK, int DV, int W, bool SCALED>
 __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd, uint8_t *R,
                                               const Rows &rw, float (&x)[8][8], Lds<DK, DV> &sm,
                                               int t, int rg, int cg, bool emit_o, size_t unit) {
@@ -426,15 +446,19 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
     // threads, threads [0, d_v) combine o while threads [d_v, 2 d_v) form the
     // scales, so the two serial combines run side by side
     constexpr int NT = DK * DV / 64;
-    if (emit_o && t < DV) A.o[unit * DV + t] = col_sum<DK, DV>(sm, t);
+    if (emit_o && t < DV) {
+        const float op = col_sum<DK, DV>(sm, t);
+        A.o[unit * DV + t] = SCALED ? sm.cf[t] * op : op;
+    }
     const int tc = (emit_o && NT >= 2 * DV) ? t - DV : t;
     if (tc >= 0 && tc < DV) {
         float ic = 1.0f;
         if (cs) {
             const float C = col_max<DK, DV>(sm, tc);
-            const uint32_t hc = h16(C);
+            const float sj = SCALED ? sm.cf[tc] : 1.0f;
+            const uint32_t hc = h16(SCALED ? C * sj : C);
             const float cv = f16v(hc);
-            ic = cv > 0.0f ? 1.0f / cv : 0.0f;
+            ic = cv > 0.0f ? sj / cv : 0.0f;
             reinterpret_cast<uint16_t *>(R + hd.cs)[tc] = (uint16_t)hc;
         }
         sm.ic[tc] = ic;
@@ -493,6 +517,11 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
     __syncthreads();
     float irr[8];
     lds_read8(&sm.ir[8 * rg], irr, 0);
+    // pivot rows among quantized rows (per-row heads only) store H(RN(x s))
+    float scc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) scc[c] = 1.0f;
+    if (SCALED && per_row<W>()) lds_read8(&sm.cf[8 * cg], scc, 0);
     bool anysat = false;
 #pragma unroll
     for (int r = 0; r < 8; ++r) anysat |= irr[r] < 0.0f;
@@ -500,13 +529,13 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         // a row step saturated at 65504: clamp codes to +-qmax
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece(x[r]));
+            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece_s<SCALED>(x[r], scc));
             else quant_row<true>(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r), fabsf(irr[r]), x[r]);
         }
     } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece(x[r]));
+            if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece_s<SCALED>(x[r], scc));
             else quant_row<false>(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r), irr[r], x[r]);
         }
     }

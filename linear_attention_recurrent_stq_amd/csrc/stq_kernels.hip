@@ -85,8 +85,11 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         sm.qf[t] = dec_io(in.q, A.io_bf16, t & 1);
     }
     if (t < DV) {
+        // column factor s: the stored column scale, or 1 (none, or a zero column)
         const float c = dec_scale(in.c, 1, t & 1);
-        sm.cf[t] = (quant && A.cs16) ? c : 1.0f;
+        const float sc = (quant && A.cs16 && c > 0.0f) ? c : 1.0f;
+        sm.cf[t] = sc;
+        sm.isf[t] = 1.0f / sc;
         vv = dec_io(in.v, A.io_bf16, t & 1);
     }
     keep_inputs(in);
@@ -96,9 +99,8 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     // Vectors are read from LDS where they are used, so that none of them is
     // held across a barrier.
     {
-        float kk[8], cc[8], s[8];
+        float kk[8], s[8];
         lds_read8(&sm.kf[8 * rg], kk, 0);
-        lds_read8(&sm.cf[8 * cg], cc, 0);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int i = 8 * rg + r;
@@ -117,10 +119,15 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
                     x[r][2 * c] = a * f16v(hv[c]);
                     x[r][2 * c + 1] = a * f16v(hv[c] >> 16);
                 }
+                if (per_row<W>()) {
+                    // a pivot row among quantized rows, in units of the column factor
+                    float is[8];
+                    lds_read8(&sm.isf[8 * cg], is, 0);
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * is[c];
+                }
             } else {
                 dequant_row(raw[r], W == kW4P ? 4 : w, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) x[r][c] = x[r][c] * cc[c];
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) s[c] = r == 0 ? x[0][c] * kk[0] : fma_(x[r][c], kk[r], s[c]);
@@ -129,7 +136,11 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         for (int c = 0; c < 8; ++c) sm.colp[c][t] = s[c];
     }
     __syncthreads();
-    if (t < DV) sm.u[t] = beta * (vv - col_sum<DK, DV>(sm, t));
+    if (t < DV) {
+        const float wv = sm.cf[t] * col_sum<DK, DV>(sm, t);
+        const float uv = beta * (vv - wv);
+        sm.u[t] = uv * sm.isf[t];
+    }
     __syncthreads();
 
     // rank-1 write, then o = S_new q partial sums
@@ -153,7 +164,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             sm.colp[c][t] = s;
         }
     }
-    requant_store<DK, DV, W>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
+    requant_store<DK, DV, W, true>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
 }
 
 
@@ -232,7 +243,7 @@ __device__ __forceinline__ void pack_tile(const Args &A, const HeadDesc &hd, uin
         x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
         x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
     }
-    requant_store<DK, DV, W>(A, hd, R, rw, x, sm, t, rg, cg, false, unit);
+    requant_store<DK, DV, W, false>(A, hd, R, rw, x, sm, t, rg, cg, false, unit);
 }
 
 template <int DK, int DV>

@@ -667,7 +667,7 @@ __device__ __forceinline__ void end_tile(const Args &A, const HeadDesc &hd, uint
     }
     __syncthreads();  // old entries are no longer read from LDS
     select_comps<DK, DV>(A, hd, R, rw, x, sm, t, rg, cg);
-    requant_store<DK, DV, W>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
+    requant_store<DK, DV, W, false>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
     if (t < DK) gmem[t] = 1.0f;
     if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = 0;
 }
@@ -749,7 +749,7 @@ __device__ __forceinline__ void pack_win_tile(const Args &A, const HeadDesc &hd,
         x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
     }
     select_comps<DK, DV>(A, hd, R, rw, x, sm, t, rg, cg);
-    requant_store<DK, DV, W>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
+    requant_store<DK, DV, W, false>(A, hd, R, rw, x, sm.b, t, rg, cg, false, unit);
     float *g = reinterpret_cast<float *>(R + hd.g);
     float *du = reinterpret_cast<float *>(R + hd.du);
     float *dkap = reinterpret_cast<float *>(R + hd.dkap);
