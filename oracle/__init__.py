@@ -35,7 +35,7 @@ class _Cfg(C.Structure):
     _fields_ = [("H", C.c_int32), ("dk", C.c_int32), ("dv", C.c_int32),
                 ("unit_keyrow", C.c_int32), ("gate_vec", C.c_int32),
                 ("rscale_f16", C.c_int32), ("cscale_f16", C.c_int32),
-                ("window", C.c_int32), ("comps", C.c_int32),
+                ("window", C.c_int32), ("comps", C.c_int32), ("scale_fit", C.c_int32),
                 ("bits", C.POINTER(C.c_uint8))]
 
 
@@ -55,6 +55,7 @@ def lib():
         L.ora_unpack_head.argtypes = [P, C.c_int, P, P]
         L.ora_pack_head.argtypes = [P, C.c_int, P, P]
         L.ora_step_head.argtypes = [P, C.c_int, P, P, P, P, P, C.c_float, P]
+        L.ora_fit_head.argtypes = [P, C.c_int, P]
         L.ora_step_f32.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P, C.c_float, P]
         L.ora_step_f64.argtypes = [C.c_int, C.c_int, C.c_int, P, P, P, P, P, C.c_double, P]
         L.ora_f32_to_f16.argtypes = [P, P, C.c_size_t]
@@ -74,14 +75,15 @@ class Cfg:
     """Oracle view of a layer: shape, storage options and per-unit widths."""
 
     def __init__(self, H, dk, dv, unit_keyrow, gate_vec, rscale_f16, cscale_f16,
-                 window, comps, bits):
+                 window, comps, bits, scale_fit=0):
         self.H, self.dk, self.dv = H, dk, dv
         self.unit_keyrow, self.gate_vec = bool(unit_keyrow), bool(gate_vec)
         self.window, self.comps = int(window), int(comps)
+        self.scale_fit = int(scale_fit)
         self.bits = np.ascontiguousarray(bits, dtype=np.uint8)
         assert self.bits.size == (H * dk if unit_keyrow else H)
         self._c = _Cfg(H, dk, dv, int(unit_keyrow), int(gate_vec), int(rscale_f16),
-                       int(cscale_f16), int(window), int(comps),
+                       int(cscale_f16), int(window), int(comps), int(scale_fit),
                        self.bits.ctypes.data_as(C.POINTER(C.c_uint8)))
         self.ptr = C.cast(C.pointer(self._c), C.c_void_p)
         self.slot_bytes = int(lib().ora_slot_bytes(self.ptr))
@@ -89,13 +91,14 @@ class Cfg:
     @classmethod
     def from_workload(cls, w, bits):
         return cls(w.H, w.dk, w.dv, w.unit == "keyrow", w.gate == "keyvec",
-                   w.row_scale == "f16", w.col_scale == "f16", w.window, w.comps, bits)
+                   w.row_scale == "f16", w.col_scale == "f16", w.window, w.comps, bits,
+                   scale_fit=1 if getattr(w, "scale_fit", "step") == "lagged" else 0)
 
     def head_layout(self, h: int) -> dict:
-        out = np.zeros(12, dtype=np.uint64)
+        out = np.zeros(16, dtype=np.uint64)
         lib().ora_head_layout(self.ptr, h, _p(out))
         keys = ["base", "codes", "rs", "cs", "wn", "g", "cidx", "cval", "du", "dkap",
-                "bytes", "nquant"]
+                "bytes", "nquant", "nrs", "ncs", "sr", "sc"]
         return {k: int(v) for k, v in zip(keys, out)}
 
     def new_slot(self) -> np.ndarray:
@@ -124,6 +127,11 @@ class Cfg:
         lib().ora_step_head(self.ptr, h, _p(slot), _p(q), _p(k), _p(v), _p(a),
                             float(np.float32(beta)), _p(o))
         return o
+
+
+    def fit_head(self, slot: np.ndarray, h: int) -> None:
+        """Lagged scales: the next scales of head h from its statistics."""
+        lib().ora_fit_head(self.ptr, h, _p(slot))
 
 
 def step_f32(M: np.ndarray, q, k, v, a, beta, gate_vec: bool) -> np.ndarray:

@@ -70,6 +70,29 @@
  * Requantizing an fp32 state M directly (pack, window end) is the same with
  * s = 1: c'_j = H(C_j), f_j = RN(1/c'_j).
  *
+ * Lagged scales (scale_fit == 1; every-step mode).  The scale fit runs apart
+ * from the decode step (STEPQuant essay, experiment-design paragraph: scale
+ * fitting and the compressed store run on a separate stream, while unpack,
+ * update and write-out are one fused kernel).  A head keeps, besides the
+ * scales r, c its codes are in, the next scales rn, cn to write with, and the
+ * statistics of its last step: SC_j (column absmax) and SR_i (row absmax in
+ * the column scale it was written with).
+ *   step, when some quantized row has rn_i > 0: the update as above, then
+ *     the statistics are the refit the every-step mode would make of this
+ *     state: SC_j = RN(max over quantized rows |M''_ij| * s_j),
+ *     SR_i = max_j |RN(M''_ij*RN(s_j/H(SC_j)))| (0 factor when H(SC_j) = 0);
+ *     the codes are written with the next scales:
+ *     f_j = cn_j > 0 ? RN(s_j/cn_j) : 0;  Z_ij = RN(M''_ij*f_j) (no column
+ *     scale: Z = M'', SR_i = max_j |M''_ij|);  irn_i = RN(1/rn_i) (0 when
+ *     rn_i = 0 or it overflows);  n'_ij = clamp(rne(Z_ij*irn_i exactly),
+ *     -qmax_i, qmax_i) -- the scales were fitted to the previous state, so
+ *     entries can clip;  pivot rows as above;  r = rn, c = cn.
+ *   step, when no quantized row has rn_i > 0 (a fresh or zero state): the
+ *     every-step refit above, with SC_j = RN(max |M''_ij| * s_j) and
+ *     SR_i = max_j |Z_ij| of that refit.
+ *   fit (a call of its own): rn_i = Hup(RN(SR_i/qmax_i)) (fp32 row scales:
+ *     RN(SR_i/qmax_i)), 0 on pivot rows;  cn_j = H(SC_j).
+ *
  * Windowed mode (window W > 1), base B_ij = RN(n_ij*r_i*c_j) (pivot: h_ij;
  * compensation positions: their fp32 value), cumulative gate g (1 at a
  * window start), deltas (u_m, kap_m), m = 1..n:
@@ -104,6 +127,7 @@ typedef struct {
     int32_t cscale_f16;     /* 1: fp16 column scales, 0: none */
     int32_t window;         /* 1: requantize every step; W > 1: windowed */
     int32_t comps;          /* K fp32 compensation entries (windowed only) */
+    int32_t scale_fit;      /* 0: scales refitted in the step; 1: lagged (fitted apart) */
     const uint8_t *bits;    /* H (per head) or H*dk (per key row) widths, 16 = pivot,
                                32 = fp32 (every-step mode only) */
 } ora_cfg;
@@ -114,6 +138,7 @@ typedef struct {
     size_t codes;           /* row bit streams, rows back to back */
     size_t rs, cs;          /* row scales, column scales (0 if absent) */
     size_t wn, g, cidx, cval, du, dkap;  /* windowed: count, gate, comps, deltas */
+    size_t nrs, ncs, sr, sc; /* lagged: next row / column scales, row / column statistics */
     size_t bytes;           /* region size */
     int32_t nquant;         /* number of quantized (4/6/8-bit) rows */
 } ora_head;
@@ -129,7 +154,10 @@ static size_t up(size_t x, size_t a) { return (x + a - 1) / a * a; }
  * a region, sections start on 16-byte boundaries in this order: codes (row i
  * takes d_v*b_i/8 bytes), row scales (if any row is quantized; d_k entries of
  * 2 or 4 bytes, 0 for pivot rows), column scales (if any row is quantized and
- * column scales are on; d_v x fp16), then for W > 1: int32 delta count,
+ * column scales are on; d_v x fp16), for lagged scales (if any row is
+ * quantized): next row scales (as the row scales), next column scales (if
+ * column scales are on), row statistics [d_k] fp32, column statistics [d_v]
+ * fp32 (if column scales are on), then for W > 1: int32 delta count,
  * g [d_k] fp32, comp index [K] uint16, comp value [K] fp32, delta values
  * [W][d_v] fp32, delta keys [W][d_k] fp32.
  */
@@ -153,6 +181,20 @@ static size_t head_layout(const ora_cfg *c, int h, size_t base, ora_head *o) {
             o->cs = p;
             p = up(p + (size_t)c->dv * 2, 16);
         }
+        if (c->scale_fit == 1) {
+            o->nrs = p;
+            p = up(p + (size_t)c->dk * (c->rscale_f16 ? 2 : 4), 16);
+            if (c->cscale_f16) {
+                o->ncs = p;
+                p = up(p + (size_t)c->dv * 2, 16);
+            }
+            o->sr = p;
+            p = up(p + (size_t)c->dk * 4, 16);
+            if (c->cscale_f16) {
+                o->sc = p;
+                p = up(p + (size_t)c->dv * 4, 16);
+            }
+        }
     }
     if (c->window > 1) {
         o->wn = p;      p = up(p + 4, 16);
@@ -173,15 +215,16 @@ size_t ora_slot_bytes(const ora_cfg *c) {
     return base;
 }
 
-/* out[0..11] = base, codes, rs, cs, wn, g, cidx, cval, du, dkap, bytes, nquant */
+/* out[0..15] = base, codes, rs, cs, wn, g, cidx, cval, du, dkap, bytes, nquant,
+ * nrs, ncs, sr, sc */
 static void get_head(const ora_cfg *c, int h, ora_head *o);
 
 void ora_head_layout(const ora_cfg *c, int h, uint64_t *out) {
     ora_head hd;
     get_head(c, h, &hd);
-    size_t v[12] = {hd.base, hd.codes, hd.rs, hd.cs, hd.wn, hd.g, hd.cidx, hd.cval,
-                    hd.du, hd.dkap, hd.bytes, (size_t)hd.nquant};
-    for (int t = 0; t < 12; ++t) out[t] = v[t];
+    size_t v[16] = {hd.base, hd.codes, hd.rs, hd.cs, hd.wn, hd.g, hd.cidx, hd.cval,
+                    hd.du, hd.dkap, hd.bytes, (size_t)hd.nquant, hd.nrs, hd.ncs, hd.sr, hd.sc};
+    for (int t = 0; t < 16; ++t) out[t] = v[t];
 }
 
 static void get_head(const ora_cfg *c, int h, ora_head *o) {
@@ -296,6 +339,8 @@ typedef struct {
     uint16_t *cidx;  /* K */
     float *cval;     /* K */
     float *du, *dkap;/* W*dv, W*dk */
+    float *nr, *nc;  /* lagged: next row / column scales (dk, dv) */
+    float *sR, *sC;  /* lagged: row / column statistics (dk, dv) */
 } ora_unit;
 
 static void unit_alloc(const ora_cfg *c, ora_unit *u) {
@@ -311,12 +356,17 @@ static void unit_alloc(const ora_cfg *c, ora_unit *u) {
     u->cval = calloc((size_t)(c->comps + 1), sizeof(float));
     u->du = calloc((size_t)c->window * c->dv, sizeof(float));
     u->dkap = calloc((size_t)c->window * c->dk, sizeof(float));
+    u->nr = calloc((size_t)c->dk, sizeof(float));
+    u->nc = calloc((size_t)c->dv, sizeof(float));
+    u->sR = calloc((size_t)c->dk, sizeof(float));
+    u->sC = calloc((size_t)c->dv, sizeof(float));
     u->nd = 0;
 }
 
 static void unit_free(ora_unit *u) {
     free(u->n); free(u->hv); free(u->fv); free(u->bw); free(u->r); free(u->c); free(u->g);
     free(u->cidx); free(u->cval); free(u->du); free(u->dkap);
+    free(u->nr); free(u->nc); free(u->sR); free(u->sC);
 }
 
 static void unit_read(const ora_cfg *c, int h, const uint8_t *slot, ora_unit *u) {
@@ -343,6 +393,16 @@ static void unit_read(const ora_cfg *c, int h, const uint8_t *slot, ora_unit *u)
     }
     for (int j = 0; j < c->dv; ++j)
         u->c[j] = (hd.nquant > 0 && c->cscale_f16) ? f16_val(rdh(R + hd.cs + 2 * (size_t)j)) : 1.0f;
+    if (c->scale_fit == 1 && hd.nquant > 0) {
+        for (int i = 0; i < c->dk; ++i) {
+            u->nr[i] = c->rscale_f16 ? f16_val(rdh(R + hd.nrs + 2 * (size_t)i)) : rdf(R + hd.nrs + 4 * (size_t)i);
+            u->sR[i] = rdf(R + hd.sr + 4 * (size_t)i);
+        }
+        for (int j = 0; j < c->dv; ++j) {
+            u->nc[j] = c->cscale_f16 ? f16_val(rdh(R + hd.ncs + 2 * (size_t)j)) : 1.0f;
+            u->sC[j] = c->cscale_f16 ? rdf(R + hd.sc + 4 * (size_t)j) : 0.0f;
+        }
+    }
     if (c->window > 1) {
         u->nd = rdi(R + hd.wn);
         for (int i = 0; i < c->dk; ++i) u->g[i] = rdf(R + hd.g + 4 * (size_t)i);
@@ -379,6 +439,18 @@ static void unit_write(const ora_cfg *c, int h, uint8_t *slot, const ora_unit *u
         }
         if (c->cscale_f16)
             for (int j = 0; j < c->dv; ++j) wrh(R + hd.cs + 2 * (size_t)j, H(u->c[j]));
+        if (c->scale_fit == 1) {
+            for (int i = 0; i < c->dk; ++i) {
+                if (c->rscale_f16) wrh(R + hd.nrs + 2 * (size_t)i, H(u->nr[i]));
+                else wrf(R + hd.nrs + 4 * (size_t)i, u->nr[i]);
+                wrf(R + hd.sr + 4 * (size_t)i, u->sR[i]);
+            }
+            if (c->cscale_f16)
+                for (int j = 0; j < c->dv; ++j) {
+                    wrh(R + hd.ncs + 2 * (size_t)j, H(u->nc[j]));
+                    wrf(R + hd.sc + 4 * (size_t)j, u->sC[j]);
+                }
+        }
     }
     if (c->window > 1) {
         wri(R + hd.wn, u->nd);
@@ -427,6 +499,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const floa
             float a = fabsf(M[e]);
             if (a > C) C = a;
         }
+        u->sC[j] = C * sj;
         u->c[j] = f16_val(H(C * sj));
         f[j] = u->c[j] > 0.0f ? sj / u->c[j] : 0.0f;
     }
@@ -451,6 +524,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const floa
             if (a > R) R = a;
         }
         int qm = qmax_of(u->bw[i]);
+        u->sR[i] = R;
         float rq = R / (float)qm;
         u->r[i] = c->rscale_f16 ? f16_val(Hup(rq)) : rq;
         float ir = u->r[i] > 0.0f ? 1.0f / u->r[i] : 0.0f;
@@ -467,6 +541,63 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const floa
     }
     free(f);
     free(Z);
+}
+
+/* Lagged scales: quantize the working state M'' (column j in units of s[j])
+ * with the next scales u->nr, u->nc fitted to the previous state, clamping to
+ * +-qmax; record the refit statistics of this state (the every-step refit's
+ * column absmax and row absmax); the next scales become the scales of the
+ * codes. */
+static void quantize_lagged(const ora_cfg *c, ora_unit *u, const float *M, const float *s) {
+    int dk = c->dk, dv = c->dv;
+    float *f = malloc(sizeof(float) * (size_t)dv);
+    float *ff = malloc(sizeof(float) * (size_t)dv);
+    for (int j = 0; j < dv; ++j) {
+        if (!c->cscale_f16) { f[j] = 1.0f; ff[j] = 1.0f; u->sC[j] = 0.0f; continue; }
+        float C = 0.0f;
+        for (int i = 0; i < dk; ++i) {
+            if (u->bw[i] >= 16) continue;
+            float a = fabsf(M[(size_t)i * dv + j]);
+            if (a > C) C = a;
+        }
+        u->sC[j] = C * s[j];
+        float cfit = f16_val(H(u->sC[j]));
+        ff[j] = cfit > 0.0f ? s[j] / cfit : 0.0f;
+        f[j] = u->nc[j] > 0.0f ? s[j] / u->nc[j] : 0.0f;
+    }
+    for (int i = 0; i < dk; ++i) {
+        if (u->bw[i] >= 16) {
+            u->r[i] = 0.0f;
+            u->sR[i] = 0.0f;
+            for (int j = 0; j < dv; ++j) {
+                size_t e = (size_t)i * dv + j;
+                if (u->bw[i] == 32) u->fv[e] = M[e] * s[j];
+                else u->hv[e] = H(M[e] * s[j]);
+                u->n[e] = 0;
+            }
+            continue;
+        }
+        int qm = qmax_of(u->bw[i]);
+        float ir = u->nr[i] > 0.0f ? 1.0f / u->nr[i] : 0.0f;
+        if (isinf(ir)) ir = 0.0f;
+        float R = 0.0f;
+        for (int j = 0; j < dv; ++j) {
+            size_t e = (size_t)i * dv + j;
+            float Zf = c->cscale_f16 ? M[e] * ff[j] : M[e];
+            if (fabsf(Zf) > R) R = fabsf(Zf);
+            float Z = c->cscale_f16 ? M[e] * f[j] : M[e];
+            double x = rint((double)Z * (double)ir);
+            if (x > qm) x = qm;
+            if (x < -qm) x = -qm;
+            u->n[e] = (int32_t)x;
+            u->hv[e] = 0;
+        }
+        u->sR[i] = R;
+        u->r[i] = u->nr[i];
+    }
+    for (int j = 0; j < dv; ++j) u->c[j] = c->cscale_f16 ? u->nc[j] : 1.0f;
+    free(f);
+    free(ff);
 }
 
 /* Top-K |M| among entries of non-pivot rows; ties to the lower column-major
@@ -553,6 +684,11 @@ void ora_pack_head(const ora_cfg *c, int h, uint8_t *slot, const float *M) {
         memset(u.dkap, 0, sizeof(float) * (size_t)c->window * c->dk);
     }
     requantize(c, &u, M, NULL, skip);
+    if (c->scale_fit == 1) {
+        /* lagged scales: no next scales yet, so the next step refits in the step */
+        memset(u.nr, 0, sizeof(float) * (size_t)c->dk);
+        memset(u.nc, 0, sizeof(float) * (size_t)c->dv);
+    }
     unit_write(c, h, slot, &u);
     free(skip);
     unit_free(&u);
@@ -599,7 +735,11 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
             }
         }
         for (int j = 0; j < dv; ++j) o[j] = sc[j] * csum(M + j, (size_t)dv, q, dk);
-        requantize(c, &u, M, sc, NULL);
+        int fitted = 0;   /* lagged scales: some quantized row has a next scale */
+        if (c->scale_fit == 1)
+            for (int i = 0; i < dk; ++i) fitted |= u.bw[i] < 16 && u.nr[i] > 0.0f;
+        if (fitted) quantize_lagged(c, &u, M, sc);
+        else requantize(c, &u, M, sc, NULL);
         free(A);
         free(sc);
         free(is);
@@ -662,6 +802,22 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
     unit_write(c, h, slot, &u);
     free(M);
     free(ai);
+    unit_free(&u);
+}
+
+/* Lagged scales: the next scales of head h from its statistics. */
+void ora_fit_head(const ora_cfg *c, int h, uint8_t *slot) {
+    if (c->scale_fit != 1) return;
+    ora_unit u;
+    unit_alloc(c, &u);
+    unit_read(c, h, slot, &u);
+    for (int i = 0; i < c->dk; ++i) {
+        if (u.bw[i] >= 16) { u.nr[i] = 0.0f; continue; }
+        float rq = u.sR[i] / (float)qmax_of(u.bw[i]);
+        u.nr[i] = c->rscale_f16 ? f16_val(Hup(rq)) : rq;
+    }
+    for (int j = 0; j < c->dv; ++j) u.nc[j] = c->cscale_f16 ? f16_val(H(u.sC[j])) : 1.0f;
+    unit_write(c, h, slot, &u);
     unit_free(&u);
 }
 

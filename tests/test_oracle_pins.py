@@ -752,3 +752,178 @@ def test_inputs_regenerate_per_unit():
     med = np.median(np.abs(M0))
     big = np.abs(M0) > 5 * med
     assert 5 <= big.any(axis=1).sum() <= 128 and big.sum() < 0.2 * M0.size
+
+
+# ------------------------------------------------------------ lagged scales
+
+def _lagged_cfg(ora, width, kda, scales, dk=32, dv=32):
+    rf16, cf16 = SCALES[scales]
+    bits = np.full(dk, width, np.uint8)
+    if kda:
+        bits[[3, 20]] = 16
+        return ora.Cfg(1, dk, dv, True, True, rf16, cf16, 1, 0, bits, scale_fit=1), bits
+    return ora.Cfg(1, dk, dv, False, False, rf16, cf16, 1, 0, bits[:1], scale_fit=1), bits
+
+
+def _read_lagged(slot, lay, dk, dv, rf16, cf16):
+    b = lay["base"]
+    nr = (slot[b + lay["nrs"]:b + lay["nrs"] + 2 * dk].view(np.float16).astype(np.float64) if rf16
+          else slot[b + lay["nrs"]:b + lay["nrs"] + 4 * dk].view(np.float32).astype(np.float64))
+    nc = (slot[b + lay["ncs"]:b + lay["ncs"] + 2 * dv].view(np.float16).astype(np.float64) if cf16
+          else np.ones(dv))
+    sr = slot[b + lay["sr"]:b + lay["sr"] + 4 * dk].view(np.float32).astype(np.float64)
+    sc = (slot[b + lay["sc"]:b + lay["sc"] + 4 * dv].view(np.float32).astype(np.float64) if cf16
+          else None)
+    return nr, nc, sr, sc
+
+
+def _smallest_f16_not_below(x):
+    h = np.asarray(x, np.float32).astype(np.float16)
+    up = h.astype(np.float64) < x
+    h[up] = np.nextafter(h[up], np.float16(np.inf))
+    return h.astype(np.float64)
+
+
+@pytest.mark.parametrize("scales", list(SCALES))
+@pytest.mark.parametrize("width", [4, 6, 8])
+@pytest.mark.parametrize("kda", [False, True])
+def test_lagged_step_against_the_exact_step(ora, width, kda, scales):
+    """Lagged scales, element by element against the exact (fp64) step of the
+    stored state: the step writes with the scales fitted from the previous
+    state's statistics (they become the stored scales); each quantized entry
+    is within half a step of the exact value, or, where the exact value lies
+    beyond qmax + 1/2 steps, stored at +-qmax with its sign (clipped); pivot
+    rows within half an fp16 ulp; o is the exact output.  The statistics are
+    the exact state's column absmax and its row absmax in the fp16 of that
+    column absmax (the every-step refit of the state); the fit gives the numpy
+    fp16 of the column statistic
+    and the smallest fp16 (or the fp32, for fp32 row scales) not below the
+    row statistic over qmax."""
+    rf16, cf16 = SCALES[scales]
+    rng = np.random.default_rng(80 + width + 3 * kda + 7 * rf16)
+    dk = dv = 32
+    cfg, bits = _lagged_cfg(ora, width, kda, scales, dk, dv)
+    qm = (1 << (width - 1)) - 1
+    piv = bits == 16
+    lay = cfg.head_layout(0)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, (rng.standard_normal((dk, dv)) * 0.5).astype(np.float32))
+    clipped_seen = 0
+    for t in range(16):
+        prev = cfg.unpack_head(slot, 0).astype(np.float64)
+        nr0, nc0, _, _ = _read_lagged(slot, lay, dk, dv, rf16, cf16)
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+        v = rng.standard_normal(dv) * (3.0 if t % 5 == 4 else 1.0)   # now and then a jump
+        a = rng.uniform(0.85, 1.0, dk if kda else 1)
+        b = rng.uniform(0.3, 1.0)
+        k, q, v, a = (x.astype(np.float32) for x in (k, q, v, a))
+        o = cfg.step_head(slot, 0, q, k, v, a, b)
+        exact = prev.copy()
+        o64 = ora.step_f64(exact, q, k, v, a, float(np.float32(b)), kda)
+        assert np.max(np.abs(o - o64)) <= 1e-5 * np.max(np.abs(o64)) + 1e-7, t
+        n, hv, r, c = slotcodec.read_head(slot, lay, bits, dk, dv, rf16, cf16)
+        new = cfg.unpack_head(slot, 0).astype(np.float64)
+        nr, nc, sr, sc = _read_lagged(slot, lay, dk, dv, rf16, cf16)
+        if t > 0:
+            # written with the scales fitted before the step
+            assert np.array_equal(r[~piv].astype(np.float64), nr0[~piv]), t
+            if cf16:
+                assert np.array_equal(c.astype(np.float64), nc0), t
+        step = np.outer(r.astype(np.float64), c.astype(np.float64))
+        slack = 1e-6 * np.abs(exact).max() + 1e-30
+        inside = np.abs(exact) <= (qm + 0.5) * step
+        q_ok = np.where(inside, np.abs(new - exact) <= 0.5 * step * (1 + 1e-5) + slack,
+                        (np.abs(n) == qm) & (np.sign(n) == np.sign(exact)))
+        p_ok = np.abs(new - exact) <= 2.0 ** -11 * np.abs(exact) + slack
+        assert np.all(np.where(piv[:, None], p_ok, q_ok)), t
+        clipped_seen += int((~inside & ~piv[:, None]).sum())
+        # statistics of the exact state
+        qrows = ~piv
+        if cf16:
+            want_c = np.abs(exact[qrows]).max(axis=0)
+            assert np.all(np.abs(sc - want_c) <= 1e-5 * want_c.max() + 1e-30), t
+            cfit = sc.astype(np.float32).astype(np.float16).astype(np.float64)
+            Zx = exact / np.where(cfit > 0, cfit, np.inf)[None, :]
+        else:
+            Zx = exact
+        want_r = np.where(qrows, np.abs(Zx).max(axis=1), 0.0)
+        assert np.all(np.abs(sr - want_r) <= 1e-5 * want_r.max() + 1e-30), t
+        # the fit
+        cfg.fit_head(slot, 0)
+        nr, nc, sr2, sc2 = _read_lagged(slot, lay, dk, dv, rf16, cf16)
+        assert np.array_equal(sr2, sr)
+        if cf16:
+            assert np.array_equal(nc, sc.astype(np.float32).astype(np.float16).astype(np.float64)), t
+        if rf16:
+            assert np.array_equal(nr[qrows], _smallest_f16_not_below(sr[qrows] / qm)), t
+        else:
+            assert np.all(np.abs(nr[qrows] - sr[qrows] / qm) <= 2.0 ** -24 * nr[qrows]), t
+        assert np.all(nr[piv] == 0)
+    assert clipped_seen > 0, "the jumps should make the lagged scales clip somewhere"
+
+
+@pytest.mark.parametrize("kda", [False, True])
+def test_lagged_first_step_is_the_every_step_refit(ora, kda):
+    """A state without fitted next scales (fresh, or just packed) is refitted
+    in the step: its first step is bit for bit the every-step mode's."""
+    rng = np.random.default_rng(90 + kda)
+    dk = dv = 32
+    lag, bits = _lagged_cfg(ora, 4, kda, "f16", dk, dv)
+    per = ora.Cfg(1, dk, dv, kda, kda, True, True, 1, 0, bits if kda else bits[:1])
+    for packed in (False, True):
+        s1, s2 = lag.new_slot(), per.new_slot()
+        if packed:
+            M0 = (rng.standard_normal((dk, dv)) * 0.5).astype(np.float32)
+            lag.pack_head(s1, 0, M0)
+            per.pack_head(s2, 0, M0)
+        k = rng.standard_normal(dk).astype(np.float32)
+        q = rng.standard_normal(dk).astype(np.float32)
+        v = rng.standard_normal(dv).astype(np.float32)
+        a = rng.uniform(0.8, 1.0, dk if kda else 1).astype(np.float32)
+        o1 = lag.step_head(s1, 0, q, k, v, a, 0.6)
+        o2 = per.step_head(s2, 0, q, k, v, a, 0.6)
+        assert np.array_equal(o1, o2)
+        h1 = slotcodec.read_head(s1, lag.head_layout(0), bits, dk, dv, True, True)
+        h2 = slotcodec.read_head(s2, per.head_layout(0), bits, dk, dv, True, True)
+        for x, y in zip(h1, h2):
+            assert np.array_equal(x, y)
+
+
+def test_lagged_scales_catch_up(ora):
+    """A state that stops changing (gate 1, write strength 0) after a jump:
+    the step of the jump clips (its scales were fitted before the jump) far
+    beyond the range, and so does the next step (it writes the clipped state
+    with scales fitted to the unclipped one); from the third step after it,
+    entries exceed the range by less than one step (a row maximum that lands
+    on the other side of a rounding boundary of the new grid) and every row
+    again spans at least 90 % of its code range."""
+    rng = np.random.default_rng(95)
+    dk = dv = 32
+    qm = 127
+    cfg, bits = _lagged_cfg(ora, 8, False, "f16", dk, dv)
+    lay = cfg.head_layout(0)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, (rng.standard_normal((dk, dv)) * 0.1).astype(np.float32))
+    ones = np.ones(1, np.float32)
+    k = np.eye(dk, dtype=np.float32)[5]
+    z = np.zeros(dv, np.float32)
+    cfg.step_head(slot, 0, k, k, z, ones, 0.0)   # refit in the step
+    cfg.fit_head(slot, 0)
+    # the jump: a large value row written along key 5
+    prev = cfg.unpack_head(slot, 0).astype(np.float64)
+    v = (rng.standard_normal(dv) * 20).astype(np.float32)
+    cfg.step_head(slot, 0, k, k, v, ones, 1.0)
+    exact = prev.copy()
+    ora.step_f64(exact, k, k, v, ones, 1.0, False)
+    n, _, r, c = slotcodec.read_head(slot, lay, bits, dk, dv, True, True)
+    assert (np.abs(exact) > (qm + 0.5) * np.outer(r, c)).sum() > dv // 2   # the jump clipped
+    cfg.fit_head(slot, 0)
+    for t in range(6):
+        prev = cfg.unpack_head(slot, 0).astype(np.float64)
+        cfg.step_head(slot, 0, k, k, z, ones, 0.0)
+        cfg.fit_head(slot, 0)
+        if t >= 2:
+            n, _, r, c = slotcodec.read_head(slot, lay, bits, dk, dv, True, True)
+            assert np.all(np.abs(prev) <= (qm + 1.0) * np.outer(r, c) * (1 + 1e-6)), t
+            assert np.all(np.abs(n).max(axis=1) >= 0.9 * qm), t
