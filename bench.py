@@ -51,6 +51,9 @@ def state_bytes(w: synth.Workload, bits: np.ndarray) -> list[int]:
         codes = int(sum(w.dv * int(b) // 8 for b in wid))
         nq = int((wid < 16).sum())  # quantized rows (not fp16 pivots or fp32 rows)
         scales = (w.dk * (2 if w.row_scale == "f16" else 4) + (2 * w.dv if w.col_scale == "f16" else 0)) if nq else 0
+        if nq and getattr(w, "scale_fit", "step") == "lagged":
+            # next scales (read by the step) and statistics (written by it)
+            scales += scales + 4 * w.dk + (4 * w.dv if w.col_scale == "f16" else 0)
         out.append(codes + scales)
     return out
 
@@ -227,15 +230,30 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    # lagged scales: each layer's scale fit runs on a second stream (default
+    # priority), after that layer's decode step and before its next one
+    lagged = getattr(w, "scale_fit", "step") == "lagged"
+    side = torch.cuda.Stream() if lagged else None
+    dec_done = [torch.cuda.Event() for _ in layers]
+    fit_done = [None for _ in layers]
 
     def one_step(t, evs=None):
         r = t % RING
         for l, (L, pool, _) in enumerate(layers):
+            if fit_done[l] is not None:
+                stream.wait_event(fit_done[l])
             if evs is not None:
                 evs[l][0].record(stream)
             stq.decode_step(pool, ids, qs[r], ks[r], vs[r], as_[r], bs[r], o, stream=stream)
             if evs is not None:
                 evs[l][1].record(stream)
+            if lagged:
+                dec_done[l].record(stream)
+                side.wait_event(dec_done[l])
+                stq.fit_scales(pool, ids, stream=side)
+                if fit_done[l] is None:
+                    fit_done[l] = torch.cuda.Event()
+                fit_done[l].record(side)
 
     # warm-up: W steps, then whole steps until the time budget has passed
     t0 = time.perf_counter()
@@ -303,6 +321,7 @@ def main() -> int:
             "unit_bits": {str(b): int(c) for b, c in zip(*np.unique(layers[0][2], return_counts=True))},
             "scales": f"row {w.row_scale}, column {w.col_scale}", "io": w.io, "window": w.window,
             "comps": w.comps, "parallelism": "single GPU",
+            "scale_fit": getattr(w, "scale_fit", "step") + (" (fit on a second stream)" if lagged else ""),
         },
         "tokens_per_s": round(w.B * K / (total_ms * 1e-3), 1),
         "hbm_gbs": round(achieved, 1),

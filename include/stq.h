@@ -52,6 +52,7 @@ typedef enum {
 enum { STQ_UNIT_HEAD = 0, STQ_UNIT_KEYROW = 1 };      /* quantization unit */
 enum { STQ_GATE_SCALAR = 0, STQ_GATE_KEYVEC = 1 };    /* gate a: [B,H] or [B,H,d_k] */
 enum { STQ_NONE = 0, STQ_F32 = 1, STQ_F16 = 2, STQ_BF16 = 3 };
+enum { STQ_FIT_STEP = 0, STQ_FIT_LAGGED = 1 };       /* where the scales are fitted */
 
 /* Layer configuration.  unit_bits is read during stq_pack_layout only. */
 typedef struct {
@@ -64,6 +65,10 @@ typedef struct {
     int32_t io_dtype;        /* q, k, v: STQ_BF16 | STQ_F32 (o is always fp32) */
     int32_t window;          /* 1: requantize every step; 2..16: windowed */
     int32_t comps;           /* windowed: K fp32 compensation entries, 0..1024 */
+    int32_t scale_fit;       /* STQ_FIT_STEP: scales refitted inside each step;
+                                STQ_FIT_LAGGED: the step writes with scales fitted
+                                to the previous state, stq_fit_scales fits the next
+                                (every-step mode, heads of one width each) */
     const uint8_t *unit_bits;/* host; H (per head) or H*d_k (per key row) widths
                                 in {4,6,8,16,32}; 16 = FP16 pivot unit; 32 = fp32
                                 (unquantized) unit: window 1 only, whole heads */
@@ -84,7 +89,8 @@ const char *stq_last_error(void);
  * stq_layout_free.  Errors: STQ_ERR_INVALID (NULL, H < 1, widths not in
  * {4,6,8,16,32}, bad enums, comps without window, comps > quantized entries),
  * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 16, fp32 units in the
- * windowed mode or on part of a head's key rows).
+ * windowed mode or on part of a head's key rows, lagged scales with the
+ * windowed mode or with key rows of different widths in one head).
  */
 stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out);
 
@@ -168,6 +174,25 @@ stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids
  */
 stq_status stq_pack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
                     const float *d_state, void *stream);
+
+/*
+ * Lagged scales (STQ_FIT_LAGGED layouts): fit the next scales of B slots from
+ * the statistics their last stq_decode_step recorded (STEPQuant essay,
+ * experiment-design paragraph: the scale fitting runs on a separate stream so
+ * that it does not block the decode path, while unpack, update and write-out
+ * are one fused kernel).  Per head with quantized rows: next column scale
+ * c~_j = H(column absmax), next row scale r~_i = smallest fp16 (fp32 row
+ * scales: the fp32) not below (row absmax in that column scale) / qmax_i.
+ * Meant for a second stream: the caller orders it after the decode step it
+ * follows (an event) and before the next decode step of the same slots.
+ * A slot that was never stepped (or was just packed) has no statistics; its
+ * next step refits in the step.
+ *   d_slot_ids [B] int32 device, distinct, in [0, slots); out-of-range ids are
+ *                       skipped
+ * Errors: STQ_ERR_INVALID (NULL pool/ids, B < 0 or B > slots, a layout
+ * without lagged scales), STQ_ERR_ALIGN, STQ_ERR_DEVICE.
+ */
+stq_status stq_fit_scales(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids, void *stream);
 
 /*
  * Host check of a batch's slot ids: every id in [0, pool->slots) and no id

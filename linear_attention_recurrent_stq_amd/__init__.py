@@ -29,17 +29,18 @@ STQ_OK, STQ_ERR_INVALID, STQ_ERR_UNSUPPORTED, STQ_ERR_TOO_SMALL, STQ_ERR_ALIGN, 
 UNIT_HEAD, UNIT_KEYROW = 0, 1
 GATE_SCALAR, GATE_KEYVEC = 0, 1
 NONE, F32, F16, BF16 = 0, 1, 2, 3
+FIT_STEP, FIT_LAGGED = 0, 1
 
 SYMBOLS = ["stq_status_string", "stq_last_error", "stq_pack_layout", "stq_layout_query",
            "stq_layout_head", "stq_layout_free", "stq_alloc_pool", "stq_decode_step",
-           "stq_unpack", "stq_pack", "stq_check_slot_ids", "stq_allocate_bits"]
+           "stq_unpack", "stq_pack", "stq_fit_scales", "stq_check_slot_ids", "stq_allocate_bits"]
 
 
 class StqConfig(C.Structure):
     _fields_ = [("H", C.c_int32), ("d_k", C.c_int32), ("d_v", C.c_int32),
                 ("unit", C.c_int32), ("gate", C.c_int32), ("row_scale", C.c_int32),
                 ("col_scale", C.c_int32), ("io_dtype", C.c_int32), ("window", C.c_int32),
-                ("comps", C.c_int32), ("unit_bits", C.POINTER(C.c_uint8))]
+                ("comps", C.c_int32), ("scale_fit", C.c_int32), ("unit_bits", C.POINTER(C.c_uint8))]
 
 
 class StqPool(C.Structure):
@@ -63,8 +64,10 @@ _lib.stq_unpack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
 _lib.stq_pack.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P, _P]
 _lib.stq_allocate_bits.argtypes = [C.c_int32, _P, _P, C.c_double, C.c_int32, _P]
 _lib.stq_check_slot_ids.argtypes = [C.POINTER(StqPool), C.c_int32, _P]
+_lib.stq_fit_scales.argtypes = [C.POINTER(StqPool), C.c_int32, _P, _P]
 for _f in ("stq_pack_layout", "stq_layout_query", "stq_layout_head", "stq_alloc_pool",
-           "stq_decode_step", "stq_unpack", "stq_pack", "stq_check_slot_ids", "stq_allocate_bits"):
+           "stq_decode_step", "stq_unpack", "stq_pack", "stq_fit_scales", "stq_check_slot_ids",
+           "stq_allocate_bits"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -90,10 +93,11 @@ class Layout:
     """stq_pack_layout: validated configuration + slot layout (host object)."""
 
     def __init__(self, H, d_k, d_v, unit_bits, *, unit=UNIT_HEAD, gate=GATE_SCALAR,
-                 row_scale=F16, col_scale=F16, io_dtype=BF16, window=1, comps=0):
+                 row_scale=F16, col_scale=F16, io_dtype=BF16, window=1, comps=0,
+                 scale_fit=FIT_STEP):
         self.unit_bits = np.ascontiguousarray(unit_bits, dtype=np.uint8)
         self.cfg = StqConfig(H, d_k, d_v, unit, gate, row_scale, col_scale, io_dtype, window,
-                             comps, self.unit_bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+                             comps, scale_fit, self.unit_bits.ctypes.data_as(C.POINTER(C.c_uint8)))
         h = _P()
         _check(_lib.stq_pack_layout(C.byref(self.cfg), C.byref(h)), "stq_pack_layout")
         self.handle = h
@@ -102,6 +106,7 @@ class Layout:
         self.slot_bytes, self.header_bytes = sb.value, hb.value
         self.H, self.d_k, self.d_v = H, d_k, d_v
         self.io_dtype, self.gate, self.window = io_dtype, gate, window
+        self.scale_fit = scale_fit
 
     @classmethod
     def from_workload(cls, w, unit_bits):
@@ -112,7 +117,8 @@ class Layout:
                    row_scale=F16 if w.row_scale == "f16" else F32,
                    col_scale=F16 if w.col_scale == "f16" else NONE,
                    io_dtype=BF16 if w.io == "bf16" else F32,
-                   window=w.window, comps=w.comps)
+                   window=w.window, comps=w.comps,
+                   scale_fit=FIT_LAGGED if getattr(w, "scale_fit", "step") == "lagged" else FIT_STEP)
 
     def head(self, h: int):
         off, nb = C.c_size_t(), C.c_size_t()
@@ -208,6 +214,15 @@ def pack(pool: Pool, slot_ids, state, stream=None) -> None:
         raise ValueError("state must be [B,H,d_k,d_v]")
     _check(_lib.stq_pack(C.byref(pool.pool), B, _dptr(slot_ids, "slot_ids", torch.int32),
                          _dptr(state, "state", torch.float32), _stream_ptr(stream)), "stq_pack")
+
+
+def fit_scales(pool: Pool, slot_ids, stream=None) -> None:
+    """stq_fit_scales: next scales of the slots from their last step's
+    statistics (lagged-scale layouts; run it on a side stream between steps)."""
+    import torch
+    _check(_lib.stq_fit_scales(C.byref(pool.pool), slot_ids.numel(),
+                               _dptr(slot_ids, "slot_ids", torch.int32), _stream_ptr(stream)),
+           "stq_fit_scales")
 
 
 def check_slot_ids(pool: "Pool", slot_ids) -> None:

@@ -96,6 +96,8 @@ struct Inputs {
     float a, beta;
     uint32_t r, k, q;  // key row t: row scale, key, query
     uint32_t c, v;     // value column t: column scale, value
+    uint32_t nr, nc;   // lagged scales: next row scale of row t % d_k, next
+                       // column scale of column t % d_v (else unused)
 };
 
 // A use of every input dword on all threads, placed once they have been
@@ -104,11 +106,20 @@ struct Inputs {
 __device__ __forceinline__ void keep_inputs(const Inputs &p) {
     asm volatile("" ::"v"(p.a), "v"(p.beta), "v"(p.r), "v"(p.k), "v"(p.q), "v"(p.c), "v"(p.v));
 }
+__device__ __forceinline__ void keep_lagged(const Inputs &p) {
+    asm volatile("" ::"v"(p.nr), "v"(p.nc));
+}
 
-template <int DK, int DV>
+template <int DK, int DV, bool LAG = false>
 __device__ __forceinline__ void fetch_inputs(const Args &A, const HeadDesc &hd, const uint8_t *R, size_t unit,
                                              int t, Inputs &p) {
     const int tk = t < DK ? t : 0, tv = t < DV ? t : 0;
+    p.nr = p.nc = 0;
+    if (LAG) {
+        // a head without these sections has offset 0 here: inside its region
+        p.nr = ld_dword(R + hd.nrs, A.rs16, t % DK);
+        p.nc = ld_dword(R + hd.ncs, 1, t % DV);
+    }
     p.beta = A.beta[unit];
     p.a = A.a[A.gate_vec ? unit * DK + tk : unit];
     // a head without scales has offset 0 here: still inside its region
@@ -456,7 +467,10 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         if (cs) {
             const float C = col_max<DK, DV>(sm, tc);
             const float sj = SCALED ? sm.cf[tc] : 1.0f;
-            const uint32_t hc = h16(SCALED ? C * sj : C);
+            const float Cs = SCALED ? C * sj : C;
+            // lagged-scale layouts record the refit statistics
+            if (A.lagged) reinterpret_cast<float *>(R + hd.scs)[tc] = Cs;
+            const uint32_t hc = h16(Cs);
             const float cv = f16v(hc);
             ic = cv > 0.0f ? sj / cv : 0.0f;
             reinterpret_cast<uint16_t *>(R + hd.cs)[tc] = (uint16_t)hc;
@@ -500,6 +514,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         bool sat = false;
         if (w != 16) {
             const float Rm = row_max<DK, DV>(sm, t);
+            if (A.lagged) reinterpret_cast<float *>(R + hd.srs)[t] = Rm;
             const float rq = Rm / (float)((1 << (w - 1)) - 1);
             if (A.rs16) {
                 rv = f16v(h16up(rq));

@@ -7,7 +7,9 @@
 // pivot rows), row scales [d_k] (fp16 or fp32) and column scales [d_v] fp16
 // when the head has a quantized row, then for the windowed mode the delta
 // count, cumulative gate g [d_k], compensation indices [K] uint16 and values
-// [K] fp32, delta values [W][d_v] and delta keys [W][d_k] (fp32).
+// [K] fp32, delta values [W][d_v] and delta keys [W][d_k] (fp32); for lagged
+// scales (when the head has a quantized row) the next row scales, next column
+// scales, row statistics [d_k] fp32 and column statistics [d_v] fp32.
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -61,6 +63,10 @@ stq_status check_cfg(const stq_config *c) {
     if (c->comps < 0 || c->comps > 1024) return fail(STQ_ERR_INVALID, "comps must be in [0, 1024]");
     if (c->window == 1 && c->comps != 0)
         return fail(STQ_ERR_INVALID, "compensation entries need the windowed mode (window > 1)");
+    if (c->scale_fit != STQ_FIT_STEP && c->scale_fit != STQ_FIT_LAGGED)
+        return fail(STQ_ERR_INVALID, "scale_fit must be STQ_FIT_STEP or STQ_FIT_LAGGED");
+    if (c->scale_fit == STQ_FIT_LAGGED && c->window != 1)
+        return fail(STQ_ERR_UNSUPPORTED, "lagged scales need the every-step mode (window 1)");
     if (!c->unit_bits) return fail(STQ_ERR_INVALID, "unit_bits is NULL");
     const size_t n = (size_t)c->H * (c->unit == STQ_UNIT_KEYROW ? c->d_k : 1);
     for (size_t i = 0; i < n; ++i) {
@@ -111,6 +117,7 @@ stq::Args base_args(const stq_pool *p, int32_t B, const int32_t *ids) {
     a.cs16 = L->cfg.col_scale == STQ_F16;
     a.window = L->cfg.window;
     a.comps = L->cfg.comps;
+    a.lagged = L->cfg.scale_fit == STQ_FIT_LAGGED;
     return a;
 }
 
@@ -239,6 +246,20 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
                 d.cs = (uint32_t)p;
                 p = up(p + (size_t)dv * 2, 16);
             }
+            if (cfg->scale_fit == STQ_FIT_LAGGED) {
+                d.nrs = (uint32_t)p;
+                p = up(p + (size_t)dk * (cfg->row_scale == STQ_F16 ? 2 : 4), 16);
+                if (cfg->col_scale == STQ_F16) {
+                    d.ncs = (uint32_t)p;
+                    p = up(p + (size_t)dv * 2, 16);
+                }
+                d.srs = (uint32_t)p;
+                p = up(p + (size_t)dk * 4, 16);
+                if (cfg->col_scale == STQ_F16) {
+                    d.scs = (uint32_t)p;
+                    p = up(p + (size_t)dv * 4, 16);
+                }
+            }
         }
         if (W > 1) {
             d.wn = (uint32_t)p;   p = up(p + 4, 16);
@@ -256,6 +277,10 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
     if (W > 1 && (size_t)K > min_quant_entries) {
         delete L;
         return fail(STQ_ERR_INVALID, "comps exceeds the quantized entries of a head");
+    }
+    if (cfg->scale_fit == STQ_FIT_LAGGED && L->mixed) {
+        delete L;
+        return fail(STQ_ERR_UNSUPPORTED, "lagged scales need heads whose key rows share one width");
     }
     L->slot_bytes = slot;
     // Head groups of the step kernel: 4-bit heads in pairs (one workgroup
@@ -354,7 +379,20 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (L->cfg.window > 1)
         return launched(stq::launch_step_win(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "windowed decode step");
+    if (L->cfg.scale_fit == STQ_FIT_LAGGED)
+        return launched(stq::launch_step_lagged(a, L->cfg.d_k, L->cfg.d_v, s), "decode step (lagged scales)");
     return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->step_mix, s), "decode step");
+}
+
+stq_status stq_fit_scales(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids, void *stream) {
+    g_err.clear();
+    if (stq_status s = check_batch(pool, B, d_slot_ids)) return s;
+    const stq_layout *L = pool->layout;
+    if (L->cfg.scale_fit != STQ_FIT_LAGGED)
+        return fail(STQ_ERR_INVALID, "the layout has no lagged scales (scale_fit is STQ_FIT_STEP)");
+    if (B == 0) return STQ_OK;
+    stq::Args a = base_args(pool, B, d_slot_ids);
+    return launched(stq::launch_fit(a, L->cfg.d_k, L->cfg.d_v, static_cast<hipStream_t>(stream)), "scale fit");
 }
 
 stq_status stq_unpack(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids, float *d_state,

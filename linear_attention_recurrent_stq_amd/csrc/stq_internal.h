@@ -16,12 +16,25 @@ struct HeadDesc {
     uint32_t bytes;    // region size
     uint32_t rs;       // row scales (valid if nquant > 0)
     uint32_t cs;       // column scales (valid if nquant > 0 and column scales on)
-    uint32_t wn;       // windowed: delta count (int32)
-    uint32_t g;        // windowed: cumulative gate [d_k] fp32
-    uint32_t cidx;     // windowed: compensation index [K] uint16
-    uint32_t cval;     // windowed: compensation value [K] fp32
-    uint32_t du;       // windowed: delta values [W][d_v] fp32
-    uint32_t dkap;     // windowed: delta keys [W][d_k] fp32
+    // The windowed sections and the lagged-scale sections never share a
+    // layout, so they share these six offsets.
+    union {
+        struct {
+            uint32_t wn;       // windowed: delta count (int32)
+            uint32_t g;        // windowed: cumulative gate [d_k] fp32
+            uint32_t cidx;     // windowed: compensation index [K] uint16
+            uint32_t cval;     // windowed: compensation value [K] fp32
+            uint32_t du;       // windowed: delta values [W][d_v] fp32
+            uint32_t dkap;     // windowed: delta keys [W][d_k] fp32
+        };
+        struct {
+            uint32_t nrs;      // lagged: next row scales [d_k] (as the row scales)
+            uint32_t ncs;      // lagged: next column scales [d_v] fp16 (if column scales)
+            uint32_t srs;      // lagged: row statistics [d_k] fp32
+            uint32_t scs;      // lagged: column statistics [d_v] fp32 (if column scales)
+            uint32_t spare0, spare1;
+        };
+    };
     uint32_t rows;     // first entry of this head in the row table
     uint16_t width;    // width shared by every row (4/6/8/16); kW4P: 4-bit rows and
                        // FP16 pivot rows; 0: rows of other differing widths
@@ -55,6 +68,7 @@ struct Args {
     int32_t B, H, nslots;
     int32_t io_bf16, gate_vec, rs16, cs16;
     int32_t window, comps;
+    int32_t lagged;              // STQ_FIT_LAGGED layout
     const uint32_t *groups;      // step kernel: [ngroups] head groups, h1 | h2 << 16
     int32_t ngroups;             //   (h2 = 0xffff: a group of one head)
 };
@@ -63,6 +77,9 @@ struct Args {
 // head of the layout has rows of different widths; `mix`: 0 none, 1 only
 // kW4P heads, 2 other mixed heads.
 hipError_t launch_step(const Args &a, int dk, int dv, int mix, hipStream_t s);
+// Lagged scales: the step (heads of one width) and the fit of the next scales.
+hipError_t launch_step_lagged(const Args &a, int dk, int dv, hipStream_t s);
+hipError_t launch_fit(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s);
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s);
 // Windowed layouts (window > 1): stq_window.hip.

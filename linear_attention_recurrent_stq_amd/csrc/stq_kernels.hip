@@ -16,21 +16,94 @@ struct Pre4 {
     uint32_t raw[8];
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool LAG = false>
 __device__ __forceinline__ void fetch4(const Args &A, const HeadDesc &hd, const uint8_t *R, size_t unit,
                                        int t, int rg, int cg, Pre4 &p) {
     const uint8_t *base = R + (uint32_t)(8 * rg * (DV / 2) + 4 * cg);
 #pragma unroll
     for (int r = 0; r < 8; ++r) p.raw[r] = *reinterpret_cast<const uint32_t *>(base + r * (DV / 2));
-    fetch_inputs<DK, DV>(A, hd, R, unit, t, p.in);
+    fetch_inputs<DK, DV, LAG>(A, hd, R, unit, t, p.in);
+}
+
+// Lagged scales (heads of one quantized width): x, the working state in
+// units of the column factor s, is written with the next scales fitted to
+// the previous state (clamped to +-qmax: the state may have outgrown them);
+// the refit statistics of x -- the column absmax and the row absmax in the
+// fp16 of that column absmax, as the every-step refit computes them -- are
+// recorded for the scale fit.  The o partial sums are in sm.colp.  The codes
+// are written as soon as the column factors are known; the row statistics
+// take one more barrier.
+template <int DK, int DV, int W>
+__device__ __forceinline__ void lag_store(const Args &A, const HeadDesc &hd, uint8_t *R, const Rows &rw,
+                                          float (&x)[8][8], Lds<DK, DV> &sm, int t, int rg, int cg,
+                                          size_t unit, const Inputs &in) {
+    static_assert(W == 4 || W == 6 || W == 8, "lagged scales: quantized heads of one width");
+    constexpr int NT = DK * DV / 64;
+    const bool cs = A.cs16;
+    if (cs) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(x[r][c]));
+            sm.colm[c][t] = m;
+        }
+    }
+    __syncthreads();
+    if (t < DV) A.o[unit * DV + t] = sm.cf[t] * col_sum<DK, DV>(sm, t);
+    // column statistics and factors: threads [d_v, 2 d_v) beside the o combine
+    const int tc = NT >= 2 * DV ? t - DV : t;
+    if (tc >= 0 && tc < DV) {
+        float ff = 1.0f, f = 1.0f;
+        if (cs) {
+            const float sj = sm.cf[tc];
+            const float Cs = col_max<DK, DV>(sm, tc) * sj;
+            reinterpret_cast<float *>(R + hd.scs)[tc] = Cs;
+            const float cfit = f16v(h16(Cs));
+            ff = cfit > 0.0f ? sj / cfit : 0.0f;
+            // in.nc is the next scale of column t % d_v = tc
+            const float nc = dec_scale(in.nc, 1, tc & 1);
+            f = nc > 0.0f ? sj / nc : 0.0f;
+            reinterpret_cast<uint16_t *>(R + hd.cs)[tc] = (uint16_t)h16(nc);
+        }
+        sm.ic[tc] = ff;  // the refit's factor (statistics)
+        sm.u[tc] = f;    // the write factor (u is dead after the update)
+    }
+    if (t < DK) {
+        const float nr = dec_scale(in.nr, A.rs16, t & 1);
+        float ir = nr > 0.0f ? 1.0f / nr : 0.0f;
+        if (__builtin_isinf(ir)) ir = 0.0f;
+        sm.ir[t] = ir;
+        if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)h16(nr);
+        else reinterpret_cast<float *>(R + hd.rs)[t] = nr;
+    }
+    __syncthreads();
+    float ffc[8], fc[8], irr[8];
+    lds_read8(&sm.ic[8 * cg], ffc, 0);
+    lds_read8(&sm.u[8 * cg], fc, 0);
+    lds_read8(&sm.ir[8 * rg], irr, 0);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float m = 0.0f, z[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            m = fmaxf(m, fabsf(cs ? x[r][c] * ffc[c] : x[r][c]));
+            z[c] = cs ? x[r][c] * fc[c] : x[r][c];
+        }
+        sm.rowm[r][t] = m;
+        quant_row<true>(R + row_o<DV, W>(rw, r), cg, W, irr[r], z);
+    }
+    __syncthreads();
+    if (t < DK) reinterpret_cast<float *>(R + hd.srs)[t] = row_max<DK, DV>(sm, t);
 }
 
 // One state.  PRE: a 4-bit state whose inputs were fetched into p (W == 4);
-// otherwise the state's inputs are loaded here.
-template <int DK, int DV, int W, bool PRE>
+// otherwise the state's inputs are loaded here.  LAG: a lagged-scale layout.
+template <int DK, int DV, int W, bool PRE, bool LAG = false>
 __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
                                           Lds<DK, DV> &sm, int t, int rg, int cg, const Pre4 &p) {
     static_assert(!PRE || W == 4, "prefetch is for 4-bit heads");
+    constexpr bool LAGQ = LAG && (W == 4 || W == 6 || W == 8);  // lagged heads with codes
     const bool quant = has_quant<W>(hd);
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
@@ -68,7 +141,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 
     // per key row and per value column constants, computed once per state
     Inputs own;
-    if (!PRE) fetch_inputs<DK, DV>(A, hd, R, unit, t, own);
+    if (!PRE) fetch_inputs<DK, DV, LAGQ>(A, hd, R, unit, t, own);
     const Inputs &in = PRE ? p.in : own;
     const float beta = in.beta;
     float vv = 0.0f;
@@ -93,7 +166,14 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         vv = dec_io(in.v, A.io_bf16, t & 1);
     }
     keep_inputs(in);
-    __syncthreads();
+    // lagged scales: the state has next scales unless it is fresh (or packed)
+    bool fitted = false;
+    if (LAGQ) {
+        keep_lagged(in);
+        fitted = __syncthreads_or(t < DK && dec_scale(in.nr, A.rs16, t & 1) > 0.0f);
+    } else {
+        __syncthreads();
+    }
     // decay + dequantize: A_ij, row by row, with the w = (a.S) k column
     // partial sums over the thread's 8 rows accumulated as the rows come in.
     // Vectors are read from LDS where they are used, so that none of them is
@@ -164,7 +244,8 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             sm.colp[c][t] = s;
         }
     }
-    requant_store<DK, DV, W, true>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
+    if (LAGQ && fitted) lag_store<DK, DV, LAGQ ? W : 4>(A, hd, R, rw, x, sm, t, rg, cg, unit, in);
+    else requant_store<DK, DV, W, true>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
 }
 
 
@@ -176,10 +257,9 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 // are all 4-bit rows with FP16 pivot rows (kW4P), 2 if some head mixes other
 // widths; only the per-row paths a layout needs are compiled, which saves
 // registers.
-template <int DK, int DV, int MIX>
-__global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
+template <int DK, int DV, int MIX, bool LAG>
+__device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
     constexpr int CG = DV / 8;
-    __shared__ Lds<DK, DV> sm;
     // ngroups == 0: every head alone (small batches keep more workgroups)
     const int ng = A.ngroups ? A.ngroups : A.H;
     const int b = (int)(blockIdx.x / (uint32_t)ng);
@@ -203,21 +283,21 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
         const HeadDesc &hd2 = A.heads[h2];
         const size_t u2 = (size_t)b * A.H + h2;
         Pre4 p1, p2;
-        fetch4<DK, DV>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
+        fetch4<DK, DV, LAG>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
         __builtin_amdgcn_sched_barrier(0);  // keep the first state's loads ahead
-        fetch4<DK, DV>(A, hd2, S + hd2.off, u2, t, rg, cg, p2);
-        step_tile<DK, DV, 4, true>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
-        step_tile<DK, DV, 4, true>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
+        fetch4<DK, DV, LAG>(A, hd2, S + hd2.off, u2, t, rg, cg, p2);
+        step_tile<DK, DV, 4, true, LAG>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
+        step_tile<DK, DV, 4, true, LAG>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
         return;
     }
     uint8_t *R = S + hd1.off;
     Pre4 none;
     switch (head_width(hd1)) {
-        case 4: step_tile<DK, DV, 4, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 6: step_tile<DK, DV, 6, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 8: step_tile<DK, DV, 8, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 16: step_tile<DK, DV, 16, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 32: step_tile<DK, DV, 32, false>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 4: step_tile<DK, DV, 4, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 6: step_tile<DK, DV, 6, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 8: step_tile<DK, DV, 8, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 16: step_tile<DK, DV, 16, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 32: step_tile<DK, DV, 32, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case kW4P:
             if (MIX >= 1) step_tile<DK, DV, kW4P, false>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
@@ -225,6 +305,21 @@ __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
             if (MIX == 2) step_tile<DK, DV, 0, false>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
     }
+}
+
+template <int DK, int DV, int MIX>
+__global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
+    __shared__ Lds<DK, DV> sm;
+    step_groups<DK, DV, MIX, false>(A, sm);
+}
+
+// Lagged scales (heads of one width, MIX 0): held to 4 waves per SIMD, the
+// every-step kernel's occupancy.
+template <int DK, int DV>
+__global__ void __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_eu(4)))
+k_step_lag(Args A) {
+    __shared__ Lds<DK, DV> sm;
+    step_groups<DK, DV, 0, true>(A, sm);
 }
 
 // ----------------------------------------------------------- pack / unpack
@@ -244,6 +339,14 @@ __device__ __forceinline__ void pack_tile(const Args &A, const HeadDesc &hd, uin
         x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
     }
     requant_store<DK, DV, W, false>(A, hd, R, rw, x, sm, t, rg, cg, false, unit);
+    if (A.lagged && has_quant<W>(hd)) {
+        // no next scales yet: the next step refits in the step
+        if (t < DK) {
+            if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.nrs)[t] = 0;
+            else reinterpret_cast<float *>(R + hd.nrs)[t] = 0.0f;
+        }
+        if (A.cs16 && t < DV) reinterpret_cast<uint16_t *>(R + hd.ncs)[t] = 0;
+    }
 }
 
 template <int DK, int DV>
@@ -344,6 +447,35 @@ __global__ void k_gate_one(uint8_t *slots, uint64_t slot_bytes, int32_t nslots,
     }
 }
 
+// Lagged scales: the next scales of every head from its statistics, one
+// thread per key row or value column of a state: next row scale
+// Hup(RN(SR_i / qmax)) (fp32 row scales: RN), next column scale H(SC_j).
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) k_fit(Args A) {
+    constexpr int PER = DK + DV;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t unit = idx / PER;
+    if (unit >= (size_t)A.B * A.H) return;
+    const int e = (int)(idx - unit * PER);
+    const int b = (int)(unit / (size_t)A.H);
+    const int h = (int)(unit - (size_t)b * A.H);
+    const int slot = A.slot_ids[b];
+    if (slot < 0 || slot >= A.nslots) return;
+    const HeadDesc &hd = A.heads[h];
+    if (head_nquant(hd) == 0) return;
+    uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
+    if (e < DK) {
+        const int w = head_width(hd);
+        const float rq = reinterpret_cast<const float *>(R + hd.srs)[e] / (float)((1 << (w - 1)) - 1);
+        if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.nrs)[e] = (uint16_t)h16up(rq);
+        else reinterpret_cast<float *>(R + hd.nrs)[e] = rq;
+    } else if (A.cs16) {
+        const int j = e - DK;
+        reinterpret_cast<uint16_t *>(R + hd.ncs)[j] =
+            (uint16_t)h16(reinterpret_cast<const float *>(R + hd.scs)[j]);
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_dims(void (*k)(Args), const Args &a, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
@@ -386,6 +518,38 @@ hipError_t launch_step(const Args &a, int dk, int dv, int mix, hipStream_t s) {
 #undef STQ_STEP
     return hipErrorInvalidValue;
 }
+hipError_t launch_step_lagged(const Args &a, int dk, int dv, hipStream_t s) {
+#define STQ_STEP_LAG(DK_, DV_)                                                                  \
+    if (dk == DK_ && dv == DV_) {                                                               \
+        Args b = a;                                                                            \
+        if (b.B == 0) return hipSuccess;                                                       \
+        if ((size_t)b.B * b.H < kPairMinStates) b.ngroups = 0;                                 \
+        const size_t per = b.ngroups ? (size_t)b.ngroups : (size_t)b.H;                        \
+        void (*k)(Args) = k_step_lag<DK_, DV_>;                                                \
+        hipLaunchKernelGGL(k, dim3((unsigned)((size_t)b.B * per)), dim3(DK_ * DV_ / 64), 0, s, b); \
+        return hipGetLastError();                                                               \
+    }
+    STQ_STEP_LAG(128, 128)
+    STQ_STEP_LAG(64, 64)
+    STQ_STEP_LAG(128, 64)
+    STQ_STEP_LAG(64, 128)
+#undef STQ_STEP_LAG
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fit(const Args &a, int dk, int dv, hipStream_t s) {
+    if (a.B == 0) return hipSuccess;
+    const size_t n = (size_t)a.B * a.H * (size_t)(dk + dv);
+    void (*k)(Args) = dk == 128 && dv == 128 ? k_fit<128, 128>
+                      : dk == 64 && dv == 64   ? k_fit<64, 64>
+                      : dk == 128 && dv == 64  ? k_fit<128, 64>
+                      : dk == 64 && dv == 128  ? k_fit<64, 128>
+                                               : nullptr;
+    if (!k) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(const Args &a, int dk, int dv, hipStream_t s) { STQ_DISPATCH(k_pack) }
 hipError_t launch_unpack(const Args &a, int dk, int dv, hipStream_t s) { STQ_DISPATCH(k_unpack) }
 

@@ -105,6 +105,7 @@ class Workload:
     layers: int = 1
     seed: int = 0
     desc: str = ""
+    scale_fit: str = "step"  # "step" (refit inside each step) | "lagged" (fitted apart)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -140,6 +141,11 @@ WORKLOADS = {
         "serving_int6", 8, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform6", pivot_frac=0.0,
         init="zero", layers=4, desc="the serving shape with uniform 6-bit heads"),
+    "serving_lagged": Workload(
+        "serving_lagged", 9, B=512, H=32, dk=128, dv=128, T=2048, unit="head", gate="scalar",
+        row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.02,
+        init="zero", layers=4, scale_fit="lagged",
+        desc="the serving pool with lagged scales (written with the previous state's fit)"),
     "windowed_kda": Workload(
         "windowed_kda", 5, B=512, H=32, dk=128, dv=128, T=1024, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,

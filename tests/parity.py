@@ -19,14 +19,6 @@ import synth
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def rel_err(x: np.ndarray, y: np.ndarray) -> float:
-    """max_j |x_j - y_j| / max(|y_j|, 1e-3 * max|y|) (y is the oracle)."""
-    y = np.asarray(y, np.float64)
-    x = np.asarray(x, np.float64)
-    den = np.maximum(np.abs(y), 1e-3 * max(np.abs(y).max(), 1e-30))
-    return float(np.max(np.abs(x - y) / den)) if y.size else 0.0
-
-
 class Harness:
     def __init__(self, w: synth.Workload, layer: int = 0, follow=None, seed_perm: int = 1,
                  bits=None):
@@ -120,6 +112,9 @@ class Harness:
         device) and the oracle o per followed unit."""
         self.stq.decode_step(self.pool, self.slot_ids, self.q, self.k, self.v, self.a,
                              self.beta, self.o)
+        lagged = self.ocfg.scale_fit == 1
+        if lagged:
+            self.stq.fit_scales(self.pool, self.slot_ids)
         gate_vec = self.w.gate == "keyvec"
 
         def one(n):
@@ -129,6 +124,8 @@ class Harness:
             a = a if gate_vec else np.float32(a)
             o = self.ocfg.step_head(self.oslots[b], h, x_followed.q[j], x_followed.k[j],
                                     x_followed.v[j], a, x_followed.beta[j])
+            if lagged:
+                self.ocfg.fit_head(self.oslots[b], h)
             e = 0.0
             if self.shadow is not None:
                 o32 = oracle.step_f32(self.shadow[n], x_followed.q[j], x_followed.k[j],

@@ -92,7 +92,7 @@ def test_header_holds_the_head_groups(stq, name):
 ])
 def test_config_rejected(stq, field, value, status):
     bits = np.full(4, 4, np.uint8)
-    cfg = stq.StqConfig(4, 64, 64, 0, 0, stq.F16, stq.F16, stq.BF16, 1, 0,
+    cfg = stq.StqConfig(4, 64, 64, 0, 0, stq.F16, stq.F16, stq.BF16, 1, 0, stq.FIT_STEP,
                         bits.ctypes.data_as(C.POINTER(C.c_uint8)))
     setattr(cfg, field, value)
     h = C.c_void_p()
@@ -205,3 +205,41 @@ def test_debug_validate_library_loads_and_exports(stq):
     lib = C.CDLL(path)
     for name in stq.SYMBOLS:
         assert hasattr(lib, name), name
+
+
+def test_lagged_scale_validation(stq):
+    """Lagged scales need the every-step mode and heads whose key rows share a
+    width; stq_fit_scales rejects a layout without lagged scales before
+    launching anything."""
+    bits = np.full(4, 4, np.uint8)
+    with pytest.raises(stq.StqError, match="every-step"):
+        stq.Layout(4, 128, 128, bits, window=4, scale_fit=stq.FIT_LAGGED)
+    kb = np.full(4 * 128, 4, np.uint8)
+    kb[7] = 16
+    with pytest.raises(stq.StqError, match="one width"):
+        stq.Layout(4, 128, 128, kb, unit=stq.UNIT_KEYROW, gate=stq.GATE_KEYVEC, scale_fit=stq.FIT_LAGGED)
+    with pytest.raises(stq.StqError, match="scale_fit"):
+        stq.Layout(4, 128, 128, bits, scale_fit=7)
+    # uniform key rows per head (different widths across heads) are accepted
+    kb = np.repeat(np.array([4, 6, 8, 16], np.uint8), 128)
+    L = stq.Layout(4, 128, 128, kb, unit=stq.UNIT_KEYROW, gate=stq.GATE_KEYVEC, scale_fit=stq.FIT_LAGGED)
+    assert L.slot_bytes > 0
+    plain = stq.Layout(4, 128, 128, bits)
+    fake = stq.StqPool(C.c_void_p(1 << 20), 0, 4, plain.handle)
+    ids = np.zeros(1, np.int32)
+    lib = stq.library()
+    assert lib.stq_fit_scales(C.byref(fake), 0, C.c_void_p(ids.ctypes.data), None) == stq.STQ_ERR_INVALID
+    assert b"no lagged scales" in lib.stq_last_error()
+
+
+def test_lagged_layout_matches_oracle(stq, ora):
+    """Slot layout of lagged-scale heads (next scales and statistics after the
+    column scales) equals the oracle's, for fp16 and fp32 row scales, with and
+    without column scales."""
+    for rs, cs in ((stq.F16, stq.F16), (stq.F32, stq.NONE)):
+        bits = np.array([4, 6, 8, 16, 32], np.uint8)
+        L = stq.Layout(5, 128, 64, bits, row_scale=rs, col_scale=cs, scale_fit=stq.FIT_LAGGED)
+        o = ora.Cfg(5, 128, 64, False, False, rs == stq.F16, cs == stq.F16, 1, 0, bits, scale_fit=1)
+        assert L.slot_bytes == o.slot_bytes
+        for h in range(5):
+            assert L.head(h) == (o.head_layout(h)["base"], o.head_layout(h)["bytes"])

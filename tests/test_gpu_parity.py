@@ -20,13 +20,17 @@ def _harness(*a, **k):
 
 
 def _check_step(o_gpu, o_ref, follow, t, tag):
-    from tests.parity import rel_err
-    worst = 0.0
-    for n, (b, h) in enumerate(follow):
-        e = rel_err(o_gpu[n], o_ref[n])
-        worst = max(worst, e)
-        assert e <= O_TOL, f"{tag}: o mismatch at step {t}, unit (b={b}, h={h}): rel err {e:.3g}"
-    return worst
+    """Every output element within relative error O_TOL of the oracle's,
+    element by element (|x - y| <= O_TOL |y|; exact where y = 0)."""
+    x = np.asarray(o_gpu, np.float64)
+    y = np.asarray(np.stack(o_ref) if len(o_ref) else np.zeros_like(x), np.float64)
+    bad = np.abs(x - y) > O_TOL * np.abs(y)
+    if bad.any():
+        n = int(np.nonzero(bad.any(axis=1))[0][0])
+        b, h = follow[n]
+        e = float(np.max(np.abs(x[n] - y[n]) / np.maximum(np.abs(y[n]), 1e-300)))
+        raise AssertionError(f"{tag}: o mismatch at step {t}, unit (b={b}, h={h}): rel err {e:.3g}")
+    return 0.0
 
 
 def _run(w, T, follow=None, bits=None, check_slots_every=0, tag=""):
@@ -119,7 +123,7 @@ def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None,
             x = hs.load_followed(t)
             o_gpu, o_ref = hs.step(x, idx_in_x=True)
             _check_step(o_gpu, o_ref, hs.follow, t, tag)
-            if (t + 1) % 256 == 0:
+            if (t + 1) % 64 == 0:
                 print(f"[{tag}] step {t + 1} ok", flush=True)
         bad = hs.compare_slots()
         assert not bad, f"{tag}: slot bytes differ after {T} steps: {bad[:4]}"
@@ -260,9 +264,15 @@ def test_largest_head_count():
     _run_sampled(w, 6, 96, seed=31, tag="h4096")
 
 
-def test_kimi_kda_all_units_32_steps():
-    """B=256 x H=32 KDA (4-bit rows + 41 FP16 pivot rows), outlier start: every unit, 32 steps."""
-    _run(synth.WORKLOADS["kimi_kda"], 32, check_slots_every=16, tag="kimi-all")
+@pytest.mark.parametrize("half", [0, 1])
+def test_kimi_kda_all_units_all_256_steps(half):
+    """B=256 x H=32 KDA (4-bit rows + 41 FP16 pivot rows), outlier start:
+    every unit over all 256 steps (each half of the requests in its own test,
+    the whole batch on the GPU), slot bytes compared at the end."""
+    w = synth.WORKLOADS["kimi_kda"]
+    reqs = range(half * w.B // 2, (half + 1) * w.B // 2)
+    _run_sampled(w, w.T, 0, 0, follow=[(b, h) for b in reqs for h in range(w.H)],
+                 tag=f"kimi-all-{half}")
 
 
 def test_kimi_kda_sampled_units_all_256_steps():
@@ -415,6 +425,55 @@ def test_windowed_mixed_rows_d64():
     _run(w, 13, bits=bits, check_slots_every=1, tag="win-mixed")
 
 
+def test_windowed_mixed_rows_d128():
+    """Windowed mode with key rows of every width {4,6,8,16} in each d = 128
+    head (the per-row in-window and window-end kernels), W = 16, K = 82:
+    every unit of 4 x 4 states over 40 steps (two window ends), slot bytes
+    compared every 8 steps."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=4, H=4, name="win_mixed_d128")
+    rng = np.random.default_rng(6)
+    bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), w.H * w.dk, p=[0.4, 0.25, 0.25, 0.1])
+    _run(w, 40, bits=bits, check_slots_every=8, tag="win-mixed-d128")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_windowed_unequal_head_sizes(dk, dv):
+    """Windowed mode at d_k != d_v (uniform 8-bit rows, and rows of mixed
+    widths), W = 8, K = 41: every unit over 20 steps, slot bytes compared
+    every 4 steps."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=3, H=4, dk=dk, dv=dv, window=8, comps=41,
+                                              name=f"win_{dk}x{dv}")
+    _run(w, 20, check_slots_every=4, tag=f"win-{dk}x{dv}")
+    rng = np.random.default_rng(dk + dv)
+    bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), w.H * w.dk, p=[0.4, 0.25, 0.25, 0.1])
+    _run(w.with_(name=f"win_{dk}x{dv}_mixed"), 20, bits=bits, check_slots_every=4,
+         tag=f"win-{dk}x{dv}-mixed")
+
+
+@pytest.mark.parametrize("K", [300, 1024])
+def test_windowed_many_entries(K):
+    """More compensation entries than threads of a workgroup (K > 256 at
+    d = 128: the whole-state selection path and several entries per thread),
+    up to the 1024 the layout accepts: every unit of 2 x 4 states over 36
+    steps from the outlier start (two window ends), slot bytes compared every
+    4 steps."""
+    w = synth.WORKLOADS["windowed_kda"].with_(B=2, H=4, comps=K, name=f"win_k{K}")
+    _run(w, 36, check_slots_every=4, tag=f"win-k{K}")
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_mixed_row_widths_unequal_head_sizes(dk, dv):
+    """Every-step mode with rows of every width {4,6,8,16} at d_k != d_v (the
+    generic per-row path), and 4-bit rows with FP16 pivot rows (the pivot-row
+    class): every unit over 12 steps, slot bytes compared every 4 steps."""
+    w = synth.WORKLOADS["kimi_kda"].with_(B=3, H=4, dk=dk, dv=dv, name=f"kda_mixed_{dk}x{dv}")
+    rng = np.random.default_rng(3 * dk + dv)
+    bits = rng.choice(np.array([4, 6, 8, 16], np.uint8), w.H * w.dk, p=[0.4, 0.25, 0.25, 0.1])
+    _run(w, 12, bits=bits, check_slots_every=4, tag=f"kda-mixed-{dk}x{dv}")
+    bits = np.where(rng.random(w.H * w.dk) < 0.1, 16, 4).astype(np.uint8)
+    _run(w.with_(name=f"kda_4p_{dk}x{dv}"), 12, bits=bits, check_slots_every=4, tag=f"kda-4p-{dk}x{dv}")
+
+
 def test_windowed_zero_state_ties():
     """From the empty state every |M| ties at 0 in the first window's selection
     (and in pack): the lowest indices must win, exactly as in the oracle."""
@@ -521,3 +580,31 @@ def test_debug_validate_build_rejects_bad_batches():
         dbg.stq_layout_free(h)
     finally:
         hs.close()
+
+
+# ------------------------------------------------------------ lagged scales
+
+def test_lagged_scales_small_batches():
+    """Lagged scales (the step writes with scales fitted to the previous
+    state, stq_fit_scales fits the next ones): every unit, slot bytes (codes,
+    scales, next scales, statistics) compared after every step, for 4-bit
+    heads with an FP16 pivot head (serving shape, 8 requests), heads of 4, 6
+    and 8 bits from a packed outlier state, and fp32 row scales without
+    column scales at d = 64 with fp32 inputs."""
+    w = synth.WORKLOADS["serving_lagged"].with_(B=8, layers=1)
+    _run(w, 20, check_slots_every=1, tag="lagged-serving")
+    w = synth.WORKLOADS["qwen_gdn"].with_(B=6, scale_fit="lagged", init="outlier", name="qwen_lagged")
+    _run(w, 20, check_slots_every=1, tag="lagged-qwen")
+    w = synth.WORKLOADS["tiny_gdn"].with_(scale_fit="lagged", name="tiny_lagged")
+    _run(w, 16, check_slots_every=1, tag="lagged-tiny")
+
+
+def test_lagged_scales_paired_heads():
+    """Lagged scales on the paired 4-bit path (512 x 32 states, the serving
+    batch): 64 followed units over 48 steps, slot bytes compared at the end;
+    and head sizes 128 x 64 and 64 x 128 (256 x 32 states)."""
+    w = synth.WORKLOADS["serving_lagged"].with_(layers=1)
+    _run_sampled(w, 48, 64, seed=51, tag="lagged-pairs")
+    for dk, dv in ((128, 64), (64, 128)):
+        w2 = w.with_(B=256, dk=dk, dv=dv, name=f"lagged_{dk}x{dv}")
+        _run_sampled(w2, 12, 48, seed=52, tag=f"lagged-{dk}x{dv}")
