@@ -121,7 +121,7 @@ def counter_traffic(workload: str):
         return None
 
 
-def _oracle_rate(w: synth.Workload, units: int, steps: int, threads: int, seed: int):
+def _oracle_rate(w: synth.Workload, bits: np.ndarray, units: int, steps: int, threads: int, seed: int):
     """The oracle, as it stands, on `units` seeded (request, head) states of the
     workload for `steps` steps, one oracle call per state-step, over `threads`
     host threads (the oracle itself is single-threaded per call).  Returns
@@ -129,7 +129,6 @@ def _oracle_rate(w: synth.Workload, units: int, steps: int, threads: int, seed: 
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
-    bits = synth.unit_bits(w)
     cfg = oracle.Cfg.from_workload(w, bits)
     rng = np.random.default_rng(seed)
     ub = rng.integers(0, w.B, units)
@@ -153,13 +152,13 @@ def _oracle_rate(w: synth.Workload, units: int, steps: int, threads: int, seed: 
     return units * steps / dt, dt
 
 
-def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
+def cpu_baseline(w: synth.Workload, bits: np.ndarray, units: int, steps: int) -> dict:
     """The oracle on this host: all usable threads (at most 16) over disjoint
     states, and one thread on a smaller sample (head-updates/s per core)."""
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    rate, dt = _oracle_rate(w, units, steps, threads, 7)
+    rate, dt = _oracle_rate(w, bits, units, steps, threads, 7)
     u1, s1 = 64, 64
-    rate1, dt1 = _oracle_rate(w, u1, s1, 1, 8)
+    rate1, dt1 = _oracle_rate(w, bits, u1, s1, 1, 8)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -174,6 +173,33 @@ def cpu_baseline(w: synth.Workload, units: int, steps: int) -> dict:
             "single_thread": {"value": round(rate1, 1), "unit": "head-updates/s", "cores": 1,
                               "sample": f"{u1} states x {s1} steps ({u1 * s1} head-updates, "
                                         f"{dt1:.2f} s on one thread)"}}
+
+
+CAL_REQUESTS, CAL_STEPS, CAL_AVG_BITS = 32, 64, 6.0
+
+
+def allocated_widths(stq, torch, w: synth.Workload, layer: int) -> np.ndarray:
+    """Widths of an allocated workload through the product path: the library's
+    calibration pass (fp32 units) over the first CAL_REQUESTS requests for
+    CAL_STEPS steps, then stq_allocate_bits (mean CAL_AVG_BITS bits over the
+    non-pivot units, pivot_frac of the units as FP16 pivots)."""
+    B = min(CAL_REQUESTS, w.B)
+
+    def inputs(t):
+        x = synth.step_inputs(w, layer, t, np.arange(B)[:, None], np.arange(w.H)[None, :])
+        if w.io == "bf16":
+            cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+            q, k, v = cv(x.q_bits), cv(x.k_bits), cv(x.v_bits)
+        else:
+            q, k, v = (torch.from_numpy(y).cuda() for y in (x.q, x.k, x.v))
+        return q, k, v, torch.from_numpy(x.a).cuda(), torch.from_numpy(x.beta).cuda()
+
+    g, m = stq.calibrate(w.H, w.dk, w.dv, B=B, steps=CAL_STEPS, inputs=inputs,
+                         unit=stq.UNIT_KEYROW if w.unit == "keyrow" else stq.UNIT_HEAD,
+                         gate=stq.GATE_KEYVEC if w.gate == "keyvec" else stq.GATE_SCALAR,
+                         io_dtype=stq.BF16 if w.io == "bf16" else stq.F32)
+    pivots = max(1, int(round(w.pivot_frac * g.size))) if w.pivot_frac > 0 else 0
+    return stq.allocate_bits(g, m, CAL_AVG_BITS, pivots)
 
 
 def main() -> int:
@@ -205,7 +231,7 @@ def main() -> int:
     dev = "cuda"
     layers = []
     for l in range(w.layers):
-        bits = synth.unit_bits(w, l)
+        bits = allocated_widths(stq, torch, w, l) if w.bits == "allocated" else synth.unit_bits(w, l)
         L = stq.Layout.from_workload(w, bits)
         pool = stq.Pool(L, w.B)
         layers.append((L, pool, bits))
@@ -322,6 +348,9 @@ def main() -> int:
             "scales": f"row {w.row_scale}, column {w.col_scale}", "io": w.io, "window": w.window,
             "comps": w.comps, "parallelism": "single GPU",
             "scale_fit": getattr(w, "scale_fit", "step") + (" (fit on a second stream)" if lagged else ""),
+            "widths": ("calibrated: fp32-unit recurrence over %d requests x %d steps, then "
+                       "stq_allocate_bits at mean %.0f bits" % (CAL_REQUESTS, CAL_STEPS, CAL_AVG_BITS)
+                       if w.bits == "allocated" else w.bits),
         },
         "tokens_per_s": round(w.B * K / (total_ms * 1e-3), 1),
         "hbm_gbs": round(achieved, 1),
@@ -340,7 +369,7 @@ def main() -> int:
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_units, args.cpu_steps)
+        rec["cpu_baseline"] = cpu_baseline(w, layers[0][2], args.cpu_units, args.cpu_steps)
     print(json.dumps(rec), flush=True)
     return 0
 

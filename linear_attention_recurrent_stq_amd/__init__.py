@@ -247,3 +247,54 @@ def allocate_bits(gate_mean, state_msq, avg_bits: float, n_pivots: int):
                                   float(avg_bits), int(n_pivots), C.c_void_p(out.ctypes.data)),
            "stq_allocate_bits")
     return out
+
+
+def calibrate(H, d_k, d_v, *, B, steps, inputs, unit=UNIT_HEAD, gate=GATE_SCALAR,
+              io_dtype=BF16, warmup=None, device="cuda"):
+    """Calibration statistics for the lifetime-aware bit allocation (STEPQuant
+    essay, temporal-axis paragraphs: widths and pivots are chosen offline from
+    how long each unit holds memory and how large its state is).
+
+    Runs the unquantized recurrence -- a layout of fp32 units (width 32) --
+    through stq_decode_step for `steps` steps of B requests, from the zero
+    state, with ``inputs(t) -> (q, k, v, a, beta)`` device tensors shaped as
+    for decode_step.  Returns float32 arrays over the units (H for
+    STQ_UNIT_HEAD, H*d_k for STQ_UNIT_KEYROW, head-major):
+      gate_mean  the unit's gate averaged over requests and steps (a head's
+                 key-vector gates averaged over its rows);
+      state_msq  the unit's mean squared state entry, averaged over requests
+                 and the steps from `warmup` on (default steps // 2).
+    Offline tooling: the reductions are torch operations on the device; the
+    recurrence runs in the library's kernels."""
+    import torch
+    keyrow = unit == UNIT_KEYROW
+    keyvec = gate == GATE_KEYVEC
+    warmup = steps // 2 if warmup is None else warmup
+    bits = np.full(H * d_k if keyrow else H, 32, np.uint8)
+    L = Layout(H, d_k, d_v, bits, unit=unit, gate=gate, io_dtype=io_dtype)
+    pool = Pool(L, B, device=device)
+    ids = torch.arange(B, dtype=torch.int32, device=device)
+    o = torch.empty(B, H, d_v, dtype=torch.float32, device=device)
+    state = torch.empty(B, H, d_k, d_v, dtype=torch.float32, device=device)
+    gsum = torch.zeros(H, d_k if keyvec else 1, dtype=torch.float64, device=device)
+    ssum = torch.zeros(H, d_k, dtype=torch.float64, device=device)
+    n_state = 0
+    for t in range(steps):
+        q, k, v, a, beta = inputs(t)
+        decode_step(pool, ids, q, k, v, a, beta, o)
+        gsum += (a.double() if keyvec else a.double()[..., None]).sum(dim=0)
+        if t >= warmup:
+            unpack(pool, ids, state)
+            ssum += state.double().square().sum(dim=(0, 3))
+            n_state += 1
+    if n_state == 0:
+        raise ValueError("calibrate: no step at or after warmup")
+    g = (gsum / (steps * B)).cpu().numpy()               # [H, d_k] or [H, 1]
+    m = (ssum / (n_state * B * d_v)).cpu().numpy()       # [H, d_k]: per key row
+    if keyrow:
+        gate_mean = np.broadcast_to(g, (H, d_k)).reshape(-1)
+        state_msq = m.reshape(-1)
+    else:
+        gate_mean = g.mean(axis=1)
+        state_msq = m.mean(axis=1)
+    return gate_mean.astype(np.float32), state_msq.astype(np.float32)

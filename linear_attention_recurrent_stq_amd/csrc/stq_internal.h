@@ -48,10 +48,11 @@ static_assert(sizeof(HeadDesc) == 64, "HeadDesc is 64 bytes");
 // the same): such heads are stepped by a path holding one dword per row.
 constexpr uint16_t kW4P = 20;
 
-// Row table entry: (byte offset of the row inside the head region) << 5 | width.
-__host__ __device__ inline uint32_t row_entry(uint32_t off, uint32_t width) { return (off << 5) | width; }
-__host__ __device__ inline uint32_t row_off(uint32_t e) { return e >> 5; }
-__host__ __device__ inline uint32_t row_width(uint32_t e) { return e & 31u; }
+// Row table entry: (byte offset of the row inside the head region) << 6 | width
+// (widths 4, 6, 8, 16 and 32 need six bits; offsets stay below 2^26).
+__host__ __device__ inline uint32_t row_entry(uint32_t off, uint32_t width) { return (off << 6) | width; }
+__host__ __device__ inline uint32_t row_off(uint32_t e) { return e >> 6; }
+__host__ __device__ inline uint32_t row_width(uint32_t e) { return e & 63u; }
 
 // Kernel arguments (passed by value).
 struct Args {

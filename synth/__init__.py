@@ -30,7 +30,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # tensor ids of the stream keys
-T_Q, T_K, T_V, T_GATE, T_BETA, T_INIT, T_LAYOUT = 1, 2, 3, 4, 5, 6, 7
+T_Q, T_K, T_V, T_GATE, T_BETA, T_INIT, T_LAYOUT, T_GATE_OFFSET = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _mix(z: np.ndarray) -> np.ndarray:
@@ -106,6 +106,7 @@ class Workload:
     seed: int = 0
     desc: str = ""
     scale_fit: str = "step"  # "step" (refit inside each step) | "lagged" (fitted apart)
+    gate_spread: float = 0.0  # KDA: per key row fixed offset U(-spread, spread) of the gate's N(2, 1)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -146,6 +147,13 @@ WORKLOADS = {
         row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.02,
         init="zero", layers=4, scale_fit="lagged",
         desc="the serving pool with lagged scales (written with the previous state's fit)"),
+    "kda_lifetimes": Workload(
+        "kda_lifetimes", 10, B=256, H=32, dk=128, dv=128, T=256, unit="keyrow", gate="keyvec",
+        row_scale="f16", col_scale="f16", io="bf16", bits="allocated", pivot_frac=0.01,
+        init="outlier", gate_spread=3.0,
+        desc="KDA B=256 H=32 d=128 T=256, key rows of different lifetimes (fixed per-row "
+             "gate offsets), widths from a calibration pass and the lifetime-aware allocation "
+             "(mean 6 bits, 1% pivot rows)"),
     "windowed_kda": Workload(
         "windowed_kda", 5, B=512, H=32, dk=128, dv=128, T=1024, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,
@@ -184,6 +192,9 @@ def unit_bits(w: Workload, layer: int = 0) -> np.ndarray:
         bits[rest] = 32
     elif w.bits == "avg4":
         bits[rest] = 4
+    elif w.bits == "allocated":
+        raise ValueError(f"{w.name}: widths come from a calibration pass and the bit allocation, "
+                         "not from the workload")
     elif w.bits == "avg6":
         n4 = n8 = m // 3
         n6 = m - n4 - n8
@@ -237,7 +248,7 @@ def step_inputs(w: Workload, layer: int, t: int, b, h) -> StepInputs:
         x = normal(key(T_GATE), 1)[..., 0]
         a = np.exp(-_softplus(x) * 0.1).astype(np.float32)
     else:
-        y = normal(key(T_GATE), w.dk) + 2.0
+        y = normal(key(T_GATE), w.dk) + 2.0 + gate_offsets(w, layer, h)
         a = (0.8 + 0.2 * _sigmoid(y)).astype(np.float32)
     beta = _sigmoid(normal(key(T_BETA), 1)[..., 0]).astype(np.float32)
     q32, k32, v32 = (x.astype(np.float32) for x in (q, k, v))
@@ -246,6 +257,18 @@ def step_inputs(w: Workload, layer: int, t: int, b, h) -> StepInputs:
         return StepInputs(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
                           a, beta, qb, kb, vb)
     return StepInputs(q32, k32, v32, a, beta)
+
+
+def gate_offsets(w: Workload, layer: int, h) -> np.ndarray:
+    """Fixed per-key-row offset of the KDA gate's normal, U(-spread, spread),
+    one per (layer, head, row): rows with a large offset forget slowly (long
+    lifetime), rows with a negative one quickly.  [..., d_k] (zeros when the
+    workload has no spread)."""
+    h = np.asarray(h, dtype=np.int64)
+    if w.gate_spread == 0.0:
+        return np.zeros(h.shape + (w.dk,))
+    u = uniform(stream_key(w.seed, w.cid, T_GATE_OFFSET, layer, 0, h), w.dk)
+    return w.gate_spread * (2.0 * u - 1.0)
 
 
 def batch_inputs(w: Workload, layer: int, t: int) -> StepInputs:

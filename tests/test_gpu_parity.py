@@ -148,11 +148,26 @@ def test_kda_4bit_rows_with_pivot_rows():
 def test_fp32_heads():
     """fp32 (unquantized) heads: the serving shape with every head fp32, and a
     layout mixing fp32, 4/6/8-bit and FP16 pivot heads; all units, slot bytes
-    compared every few steps."""
+    compared every few steps; stq_unpack of the mixed layout, and of a
+    key-row layout whose units are all fp32 rows, equals the oracle's (a
+    width of 32 in the row table once read back as 0)."""
     _run(synth.WORKLOADS["serving_fp32"].with_(B=16), 8, check_slots_every=4, tag="fp32")
     w = synth.WORKLOADS["qwen_gdn"].with_(B=6, H=6, name="qwen_mixed_fp32")
     bits = np.array([32, 4, 16, 6, 32, 8], np.uint8)
-    _run(w, 10, bits=bits, check_slots_every=5, tag="fp32-mixed")
+    hs = _run(w, 10, bits=bits, check_slots_every=5, tag="fp32-mixed")
+    wk = synth.WORKLOADS["kimi_kda"].with_(B=3, H=4, init="zero", name="kda_fp32")
+    bk = np.full(wk.H * wk.dk, 32, np.uint8)
+    bk[wk.dk:2 * wk.dk] = 4
+    for w_, b_, steps in ((w, bits, 10), (wk, bk, 6)):
+        h2 = _harness(w_, bits=b_)
+        try:
+            for t in range(steps):
+                h2.step(h2.load_full(t))
+            got = h2.unpack_gpu()
+            for b, h in h2.follow:
+                assert np.array_equal(got[b, h], h2.ocfg.unpack_head(h2.oslots[b], h)), (w_.name, b, h)
+        finally:
+            h2.close()
 
 
 def test_qwen_gdn_all_units_all_steps():
@@ -608,3 +623,41 @@ def test_lagged_scales_paired_heads():
     for dk, dv in ((128, 64), (64, 128)):
         w2 = w.with_(B=256, dk=dk, dv=dv, name=f"lagged_{dk}x{dv}")
         _run_sampled(w2, 12, 48, seed=52, tag=f"lagged-{dk}x{dv}")
+
+
+# ------------------------------------------- calibration and allocated widths
+
+def test_calibration_matches_oracle_and_allocated_widths_step_exactly():
+    """The library's calibration pass (the fp32-unit recurrence through the C
+    ABI, statistics reduced on the device) gives the oracle's per-row gate
+    means and mean squared state entries on the KDA workload whose key rows
+    have different lifetimes (8 requests, 48 steps).  The widths the
+    allocation oracle gives for them (mean 6 bits, 1 % pivot rows) mix 4, 6,
+    8 and 16 bits in every head and favour long-lived rows; the library's
+    allocation of the same statistics is identical; and the HIP path steps
+    those widths bit for bit like the oracle: every unit of 8 requests over 24
+    steps from the outlier start, slot bytes compared every 8 steps."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    from tests.calibration import allocated_bits
+    w = synth.WORKLOADS["kda_lifetimes"]
+    B, T = 8, 48
+
+    def inputs(t):
+        x = synth.step_inputs(w, 0, t, np.arange(B)[:, None], np.arange(w.H)[None, :])
+        bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+        return (bf(x.q_bits), bf(x.k_bits), bf(x.v_bits), torch.from_numpy(x.a).cuda(),
+                torch.from_numpy(x.beta).cuda())
+
+    g_lib, m_lib = stq.calibrate(w.H, w.dk, w.dv, B=B, steps=T, inputs=inputs, unit=stq.UNIT_KEYROW,
+                                 gate=stq.GATE_KEYVEC)
+    bits, g, m = allocated_bits(w, 0, B, T)
+    np.testing.assert_allclose(g_lib, g, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(m_lib, m, rtol=1e-5, atol=0)
+    assert np.array_equal(stq.allocate_bits(g, m, 6.0, int((bits == 16).sum())), bits)
+    per_head = bits.reshape(w.H, w.dk)
+    assert sum(len(set(r.tolist())) >= 3 for r in per_head) > w.H // 2
+    lt = 1.0 / (1.0 - np.minimum(g.astype(np.float64), 1 - 2 ** -20))
+    assert np.median(lt[bits == 8]) > np.median(lt[bits == 4])
+    print(f"[allocated] widths {dict(zip(*np.unique(bits, return_counts=True)))}", flush=True)
+    _run(w.with_(B=8), 24, bits=bits, check_slots_every=8, tag="allocated")
