@@ -27,7 +27,6 @@ total risk sum_u r_u(b_u) over the assignments within the budget.
 """
 from __future__ import annotations
 
-import heapq
 import math
 
 WIDTHS = (4, 6, 8)
@@ -65,12 +64,18 @@ def allocate(gate_mean, state_msq, avg_bits: float, n_pivots: int) -> list[int]:
     rest = [u for u in range(n) if bits[u] != PIVOT]
     budget = math.floor(avg_bits * len(rest))
     used = 4 * len(rest)
-    heap = [(-gain(s[u], 4), u) for u in rest]
-    heapq.heapify(heap)
-    while heap and used + 2 <= budget:
-        _, u = heapq.heappop(heap)
-        bits[u] += 2
+    # plain greedy: scan every unit for the largest gain of its next 2 bits
+    # (a unit at 8 bits, or a pivot, offers none); the first maximum in index
+    # order wins ties
+    while used + 2 <= budget:
+        best, best_gain = -1, -1.0
+        for u in rest:
+            if bits[u] < 8:
+                gu = gain(s[u], bits[u])
+                if gu > best_gain:
+                    best, best_gain = u, gu
+        if best < 0:
+            break
+        bits[best] += 2
         used += 2
-        if bits[u] < 8:
-            heapq.heappush(heap, (-gain(s[u], bits[u]), u))
     return bits
