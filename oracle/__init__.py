@@ -36,7 +36,7 @@ class _Cfg(C.Structure):
                 ("unit_keyrow", C.c_int32), ("gate_vec", C.c_int32),
                 ("rscale_f16", C.c_int32), ("cscale_f16", C.c_int32),
                 ("window", C.c_int32), ("comps", C.c_int32), ("scale_fit", C.c_int32),
-                ("bits", C.POINTER(C.c_uint8))]
+                ("bits", C.POINTER(C.c_uint8)), ("impact", C.POINTER(C.c_float))]
 
 
 _lib = None
@@ -75,24 +75,29 @@ class Cfg:
     """Oracle view of a layer: shape, storage options and per-unit widths."""
 
     def __init__(self, H, dk, dv, unit_keyrow, gate_vec, rscale_f16, cscale_f16,
-                 window, comps, bits, scale_fit=0):
+                 window, comps, bits, scale_fit=0, row_impact=None):
         self.H, self.dk, self.dv = H, dk, dv
         self.unit_keyrow, self.gate_vec = bool(unit_keyrow), bool(gate_vec)
         self.window, self.comps = int(window), int(comps)
         self.scale_fit = int(scale_fit)
         self.bits = np.ascontiguousarray(bits, dtype=np.uint8)
         assert self.bits.size == (H * dk if unit_keyrow else H)
+        self.row_impact = None if row_impact is None else np.ascontiguousarray(row_impact, dtype=np.float32)
+        assert self.row_impact is None or self.row_impact.size == H * dk
         self._c = _Cfg(H, dk, dv, int(unit_keyrow), int(gate_vec), int(rscale_f16),
                        int(cscale_f16), int(window), int(comps), int(scale_fit),
-                       self.bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+                       self.bits.ctypes.data_as(C.POINTER(C.c_uint8)),
+                       None if self.row_impact is None
+                       else self.row_impact.ctypes.data_as(C.POINTER(C.c_float)))
         self.ptr = C.cast(C.pointer(self._c), C.c_void_p)
         self.slot_bytes = int(lib().ora_slot_bytes(self.ptr))
 
     @classmethod
-    def from_workload(cls, w, bits):
+    def from_workload(cls, w, bits, row_impact=None):
         return cls(w.H, w.dk, w.dv, w.unit == "keyrow", w.gate == "keyvec",
                    w.row_scale == "f16", w.col_scale == "f16", w.window, w.comps, bits,
-                   scale_fit=1 if getattr(w, "scale_fit", "step") == "lagged" else 0)
+                   scale_fit=1 if getattr(w, "scale_fit", "step") == "lagged" else 0,
+                   row_impact=row_impact)
 
     def head_layout(self, h: int) -> dict:
         out = np.zeros(16, dtype=np.uint64)

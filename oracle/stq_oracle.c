@@ -70,6 +70,16 @@
  * Requantizing an fp32 state M directly (pack, window end) is the same with
  * s = 1: c'_j = H(C_j), f_j = RN(1/c'_j).
  *
+ * Row-impact weighting (row_impact given; STEPQuant essay, spatial-axis
+ * paragraph: each key row's contribution to the output error is scored, and
+ * experiment-design paragraph: the column scale penalizes reconstruction
+ * error on high-impact rows, large-value rows get a wide range and important
+ * rows a finer resolution).  With impact iota_i >= 0 per key row of a head,
+ * w_i = RN(sqrt(iota_i / max_k iota_k)) (computed in double; 1 when the
+ * head's impacts are all 0), the column maximum becomes
+ * C_j = max over quantized rows RN(w_i |M''_ij|); the row scale is fitted as
+ * above, to the row's current magnitude in those column units.
+ *
  * Lagged scales (scale_fit == 1; every-step mode).  The scale fit runs apart
  * from the decode step (STEPQuant essay, experiment-design paragraph: scale
  * fitting and the compressed store run on a separate stream, while unpack,
@@ -130,6 +140,7 @@ typedef struct {
     int32_t scale_fit;      /* 0: scales refitted in the step; 1: lagged (fitted apart) */
     const uint8_t *bits;    /* H (per head) or H*dk (per key row) widths, 16 = pivot,
                                32 = fp32 (every-step mode only) */
+    const float *impact;    /* NULL, or H*dk row-impact scores >= 0 (every-step mode) */
 } ora_cfg;
 
 /* Byte offsets of one head region inside a slot. */
@@ -484,11 +495,26 @@ static void dequant_base(const ora_cfg *c, const ora_unit *u, float *B, int with
 /* Requantize into u (codes, pivots, scales) the state whose column j is
  * M[., j] * s[j] (s == NULL: all ones, M is the state itself).  skip[e] != 0
  * excludes an entry. */
-static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const float *s,
+/* Row-impact weights of head h (NULL without impact scores). */
+static float *impact_weights(const ora_cfg *c, int h) {
+    if (!c->impact) return NULL;
+    float *w = malloc(sizeof(float) * (size_t)c->dk);
+    double mx = 0.0;
+    for (int i = 0; i < c->dk; ++i) {
+        double v = c->impact[(size_t)h * c->dk + i];
+        if (v > mx) mx = v;
+    }
+    for (int i = 0; i < c->dk; ++i)
+        w[i] = mx > 0.0 ? (float)sqrt((double)c->impact[(size_t)h * c->dk + i] / mx) : 1.0f;
+    return w;
+}
+
+static void requantize(const ora_cfg *c, int h, ora_unit *u, const float *M, const float *s,
                        const uint8_t *skip) {
     int dk = c->dk, dv = c->dv;
     float *f = malloc(sizeof(float) * (size_t)dv);
     float *Z = malloc(sizeof(float) * (size_t)dk * dv);
+    float *wi = impact_weights(c, h);
     for (int j = 0; j < dv; ++j) {
         if (!c->cscale_f16) { u->c[j] = 1.0f; f[j] = 1.0f; continue; }
         float sj = s ? s[j] : 1.0f;
@@ -496,7 +522,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const floa
         for (int i = 0; i < dk; ++i) {
             size_t e = (size_t)i * dv + j;
             if (u->bw[i] >= 16 || (skip && skip[e])) continue;
-            float a = fabsf(M[e]);
+            float a = wi ? wi[i] * fabsf(M[e]) : fabsf(M[e]);
             if (a > C) C = a;
         }
         u->sC[j] = C * sj;
@@ -541,6 +567,7 @@ static void requantize(const ora_cfg *c, ora_unit *u, const float *M, const floa
     }
     free(f);
     free(Z);
+    free(wi);
 }
 
 /* Lagged scales: quantize the working state M'' (column j in units of s[j])
@@ -683,7 +710,7 @@ void ora_pack_head(const ora_cfg *c, int h, uint8_t *slot, const float *M) {
         memset(u.du, 0, sizeof(float) * (size_t)c->window * c->dv);
         memset(u.dkap, 0, sizeof(float) * (size_t)c->window * c->dk);
     }
-    requantize(c, &u, M, NULL, skip);
+    requantize(c, h, &u, M, NULL, skip);
     if (c->scale_fit == 1) {
         /* lagged scales: no next scales yet, so the next step refits in the step */
         memset(u.nr, 0, sizeof(float) * (size_t)c->dk);
@@ -739,7 +766,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
         if (c->scale_fit == 1)
             for (int i = 0; i < dk; ++i) fitted |= u.bw[i] < 16 && u.nr[i] > 0.0f;
         if (fitted) quantize_lagged(c, &u, M, sc);
-        else requantize(c, &u, M, sc, NULL);
+        else requantize(c, h, &u, M, sc, NULL);
         free(A);
         free(sc);
         free(is);
@@ -792,7 +819,7 @@ void ora_step_head(const ora_cfg *c, int h, uint8_t *slot, const float *q, const
                 }
             uint8_t *skip = calloc(e, 1);
             select_comps(c, &u, M, skip);
-            requantize(c, &u, M, NULL, skip);
+            requantize(c, h, &u, M, NULL, skip);
             for (int i = 0; i < dk; ++i) u.g[i] = 1.0f;
             u.nd = 0;   /* the stored deltas are left as they are: only n counts */
             free(skip);

@@ -927,3 +927,145 @@ def test_lagged_scales_catch_up(ora):
             n, _, r, c = slotcodec.read_head(slot, lay, bits, dk, dv, True, True)
             assert np.all(np.abs(prev) <= (qm + 1.0) * np.outer(r, c) * (1 + 1e-6)), t
             assert np.all(np.abs(n).max(axis=1) >= 0.9 * qm), t
+
+
+# ------------------------------------------------------------ row impact
+
+def _imp_cfg(ora, impact, width=8, dk=32, dv=32, H=1, keyrow=False):
+    bits = np.full(H * dk if keyrow else H, width, np.uint8)
+    return ora.Cfg(H, dk, dv, keyrow, keyrow, True, True, 1, 0, bits, row_impact=impact)
+
+
+def test_impact_equal_scores_are_the_plain_fit(ora):
+    """Equal impact scores (any positive value, or all zero) leave the fit as
+    it is without scores, bit for bit, in pack and in every step; and
+    multiplying every score of a head by a constant changes nothing."""
+    rng = np.random.default_rng(100)
+    dk = dv = 32
+    plain = _imp_cfg(ora, None)
+    imp = rng.uniform(0.1, 2.0, dk).astype(np.float32)
+    variants = [(np.full(dk, 3.5, np.float32), plain), (np.zeros(dk, np.float32), plain),
+                (imp * 7.0, _imp_cfg(ora, imp))]
+    for scores, ref in variants:
+        cfg = _imp_cfg(ora, scores)
+        s1, s2 = cfg.new_slot(), ref.new_slot()
+        M0 = (rng.standard_normal((dk, dv)) * 0.5).astype(np.float32)
+        cfg.pack_head(s1, 0, M0)
+        ref.pack_head(s2, 0, M0)
+        assert np.array_equal(s1, s2)
+        for t in range(6):
+            k, q = rng.standard_normal(dk).astype(np.float32), rng.standard_normal(dk).astype(np.float32)
+            v = rng.standard_normal(dv).astype(np.float32)
+            a = np.float32(rng.uniform(0.8, 1.0))
+            o1 = cfg.step_head(s1, 0, q, k, v, a, 0.5)
+            o2 = ref.step_head(s2, 0, q, k, v, a, 0.5)
+            assert np.array_equal(o1, o2) and np.array_equal(s1, s2), t
+
+
+def test_column_scale_follows_the_largest_rms_output_contribution(ora):
+    """An entry M_ij reaches o_j as q_i M_ij, whose RMS over queries with
+    E[q_i^2] = iota_i is sqrt(iota_i) |M_ij|.  The column scale is set by the
+    entry with the largest such contribution: with row A (impact 1, value 1)
+    and row B (impact 1/4) in one column, B sets the scale once its value
+    exceeds 2 (its contribution exceeds A's), and not before."""
+    dk = dv = 8
+    imp = np.ones(dk, np.float32)
+    imp[1] = 0.25
+    cfg = _imp_cfg(ora, imp, dk=dk, dv=dv)
+    lay = cfg.head_layout(0)
+    for yb, want in ((1.5, 1.0), (1.9, 1.0), (2.5, 1.25), (3.0, 1.5)):
+        M = np.full((dk, dv), 0.01, np.float32)
+        M[0, 3] = 1.0
+        M[1, 3] = yb
+        slot = cfg.new_slot()
+        cfg.pack_head(slot, 0, M)
+        _, _, _, c = slotcodec.read_head(slot, lay, np.full(dk, 8), dk, dv, True, True)
+        assert c[3] == np.float16(want), (yb, c[3])
+
+
+def test_zero_impact_rows_leave_the_column_scales(ora):
+    """Rows of impact 0 do not set the column scales: each column scale is
+    the numpy fp16 of the largest |M| over the other rows, however large the
+    zero-impact rows are; those rows still get their full range (no code
+    clips, every entry within half a step)."""
+    rng = np.random.default_rng(101)
+    dk = dv = 32
+    quiet = {0: [2, 9, 30], 1: [0, 17]}          # per head
+    imp = np.ones((2, dk), np.float32)
+    imp[1] *= 4.0                                 # scores are relative within a head
+    for h, rows in quiet.items():
+        imp[h, rows] = 0.0
+    cfg = _imp_cfg(ora, imp.ravel(), H=2)
+    for trial in range(5):
+        slot = cfg.new_slot()
+        Ms = []
+        for h in range(2):
+            M = rng.standard_normal((dk, dv)).astype(np.float32)
+            M[quiet[h]] *= 50.0
+            cfg.pack_head(slot, h, M)
+            Ms.append(M)
+        for h in range(2):
+            M, rows = Ms[h], quiet[h]
+            n, _, r, c = slotcodec.read_head(slot, cfg.head_layout(h), np.full(dk, 8), dk, dv, True, True)
+            rest = np.abs(np.delete(M, rows, axis=0)).max(axis=0)
+            assert np.array_equal(c, rest.astype(np.float16).astype(np.float32)), (trial, h)
+            step = np.outer(r.astype(np.float64), c.astype(np.float64))
+            assert np.all(np.abs(M) <= (127 + 0.5) * step)
+            assert np.all(np.abs(M - n * step) <= 0.5 * step * (1 + 1e-5))
+            assert np.all(np.abs(n[rows]).max(axis=1) == 127)
+
+
+def test_impact_weighted_fit_lowers_the_output_error(ora):
+    """The purpose of the weighting: when a few large entries sit in rows
+    whose query weight is small (each widens its whole column under the plain
+    absmax fit, which no row scale can undo), fitting the column scales to the
+    high-impact rows at least halves the output error
+    E|sum_i q_i (M_ij - stored_ij)|^2 for queries drawn with that impact
+    profile (E[q_i^2] = iota_i), against the plain fit of the same states; at
+    4, 6 and 8 bits."""
+    rng = np.random.default_rng(102)
+    dk = dv = 32
+    iota = np.where(np.arange(dk) < 8, 0.02, 1.0).astype(np.float32)  # 8 low-impact rows
+    for width in (4, 6, 8):
+        plain, weighted = _imp_cfg(ora, None, width), _imp_cfg(ora, iota, width)
+        err = {0: 0.0, 1: 0.0}
+        for trial in range(20):
+            M = (rng.standard_normal((dk, dv)) * 0.3).astype(np.float32)
+            for i in range(8):   # three large entries in each low-impact row
+                M[i, rng.choice(dv, 3, replace=False)] *= 50.0
+            for key, cfg in ((0, plain), (1, weighted)):
+                slot = cfg.new_slot()
+                cfg.pack_head(slot, 0, M)
+                E = cfg.unpack_head(slot, 0).astype(np.float64) - M
+                # E over q with E[q_i q_k] = iota_i delta_ik
+                err[key] += float((iota[:, None] * E ** 2).sum())
+        assert err[1] < 0.5 * err[0], (width, err)
+
+
+@pytest.mark.parametrize("width", [4, 8])
+def test_impact_weighted_step_injects_at_most_half_a_step(ora, width):
+    """With row-impact weights the step is still the exact step of the stored
+    state plus at most half a step r'_i c'_j per entry, and o is exact."""
+    rng = np.random.default_rng(103 + width)
+    dk = dv = 32
+    iota = rng.uniform(0.0, 1.0, dk).astype(np.float32) ** 3
+    cfg = _imp_cfg(ora, iota, width)
+    lay = cfg.head_layout(0)
+    slot = cfg.new_slot()
+    cfg.pack_head(slot, 0, (rng.standard_normal((dk, dv)) * 0.5).astype(np.float32))
+    for t in range(16):
+        prev = cfg.unpack_head(slot, 0).astype(np.float64)
+        k = rng.standard_normal(dk); k /= np.linalg.norm(k)
+        q = rng.standard_normal(dk); q /= np.linalg.norm(q)
+        v = rng.standard_normal(dv)
+        a = rng.uniform(0.85, 1.0, 1)
+        b = rng.uniform(0.3, 1.0)
+        k, q, v, a = (x.astype(np.float32) for x in (k, q, v, a))
+        o = cfg.step_head(slot, 0, q, k, v, a, b)
+        exact = prev.copy()
+        o64 = ora.step_f64(exact, q, k, v, a, float(np.float32(b)), False)
+        assert np.max(np.abs(o - o64)) <= 1e-5 * np.max(np.abs(o64)) + 1e-7, t
+        new = cfg.unpack_head(slot, 0).astype(np.float64)
+        _, _, r, c = slotcodec.read_head(slot, lay, np.full(dk, width), dk, dv, True, True)
+        half = 0.5 * np.outer(r.astype(np.float64), c.astype(np.float64))
+        assert np.all(np.abs(new - exact) <= half * (1 + 1e-5) + 1e-6 * np.abs(exact) + 1e-30), t
