@@ -121,7 +121,8 @@ def counter_traffic(workload: str):
         return None
 
 
-def _oracle_rate(w: synth.Workload, bits: np.ndarray, units: int, steps: int, threads: int, seed: int):
+def _oracle_rate(w: synth.Workload, bits: np.ndarray, units: int, steps: int, threads: int, seed: int,
+                 row_impact=None):
     """The oracle, as it stands, on `units` seeded (request, head) states of the
     workload for `steps` steps, one oracle call per state-step, over `threads`
     host threads (the oracle itself is single-threaded per call).  Returns
@@ -129,7 +130,7 @@ def _oracle_rate(w: synth.Workload, bits: np.ndarray, units: int, steps: int, th
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
-    cfg = oracle.Cfg.from_workload(w, bits)
+    cfg = oracle.Cfg.from_workload(w, bits, row_impact=row_impact)
     rng = np.random.default_rng(seed)
     ub = rng.integers(0, w.B, units)
     uh = rng.integers(0, w.H, units)
@@ -152,13 +153,13 @@ def _oracle_rate(w: synth.Workload, bits: np.ndarray, units: int, steps: int, th
     return units * steps / dt, dt
 
 
-def cpu_baseline(w: synth.Workload, bits: np.ndarray, units: int, steps: int) -> dict:
+def cpu_baseline(w: synth.Workload, bits: np.ndarray, units: int, steps: int, row_impact=None) -> dict:
     """The oracle on this host: all usable threads (at most 16) over disjoint
     states, and one thread on a smaller sample (head-updates/s per core)."""
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    rate, dt = _oracle_rate(w, bits, units, steps, threads, 7)
+    rate, dt = _oracle_rate(w, bits, units, steps, threads, 7, row_impact)
     u1, s1 = 64, 64
-    rate1, dt1 = _oracle_rate(w, bits, u1, s1, 1, 8)
+    rate1, dt1 = _oracle_rate(w, bits, u1, s1, 1, 8, row_impact)
     cpu = "unknown"
     try:
         for line in open("/proc/cpuinfo"):
@@ -202,6 +203,17 @@ def allocated_widths(stq, torch, w: synth.Workload, layer: int) -> np.ndarray:
     return stq.allocate_bits(g, m, CAL_AVG_BITS, pivots)
 
 
+def query_impact(w: synth.Workload, layer: int) -> np.ndarray:
+    """Row-impact scores E[q_i^2] per (head, key row) from the calibration
+    queries (the first CAL_REQUESTS requests over CAL_STEPS steps)."""
+    B = min(CAL_REQUESTS, w.B)
+    acc = np.zeros((w.H, w.dk))
+    for t in range(CAL_STEPS):
+        x = synth.step_inputs(w, layer, t, np.arange(B)[:, None], np.arange(w.H)[None, :])
+        acc += (x.q.astype(np.float64) ** 2).sum(axis=0)
+    return (acc / (B * CAL_STEPS)).reshape(-1).astype(np.float32)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,12 +241,14 @@ def main() -> int:
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     dev = "cuda"
-    layers = []
+    layers, impacts = [], []
     for l in range(w.layers):
         bits = allocated_widths(stq, torch, w, l) if w.bits == "allocated" else synth.unit_bits(w, l)
-        L = stq.Layout.from_workload(w, bits)
+        impact = query_impact(w, l) if getattr(w, "impact", "none") == "queries" else None
+        L = stq.Layout.from_workload(w, bits, row_impact=impact)
         pool = stq.Pool(L, w.B)
         layers.append((L, pool, bits))
+        impacts.append(impact)
     ids = torch.from_numpy(np.arange(w.B, dtype=np.int32)[::-1].copy()).to(dev)
 
     io = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -348,6 +362,8 @@ def main() -> int:
             "scales": f"row {w.row_scale}, column {w.col_scale}", "io": w.io, "window": w.window,
             "comps": w.comps, "parallelism": "single GPU",
             "scale_fit": getattr(w, "scale_fit", "step") + (" (fit on a second stream)" if lagged else ""),
+            "row_impact": ("E[q_i^2] over %d requests x %d calibration steps" % (CAL_REQUESTS, CAL_STEPS)
+                           if getattr(w, "impact", "none") == "queries" else None),
             "widths": ("calibrated: fp32-unit recurrence over %d requests x %d steps, then "
                        "stq_allocate_bits at mean %.0f bits" % (CAL_REQUESTS, CAL_STEPS, CAL_AVG_BITS)
                        if w.bits == "allocated" else w.bits),
@@ -369,7 +385,7 @@ def main() -> int:
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, layers[0][2], args.cpu_units, args.cpu_steps)
+        rec["cpu_baseline"] = cpu_baseline(w, layers[0][2], args.cpu_units, args.cpu_steps, impacts[0])
     print(json.dumps(rec), flush=True)
     return 0
 

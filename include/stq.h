@@ -72,6 +72,12 @@ typedef struct {
     const uint8_t *unit_bits;/* host; H (per head) or H*d_k (per key row) widths
                                 in {4,6,8,16,32}; 16 = FP16 pivot unit; 32 = fp32
                                 (unquantized) unit: window 1 only, whole heads */
+    const float *row_impact; /* host, NULL or [H*d_k] row-impact scores >= 0 (STEPQuant
+                                essay, spatial-axis paragraph), fixed offline: the
+                                column scales are fitted to max_i w_i |M_ij| with
+                                w_i = sqrt(score_i / the head's largest score) (1 when
+                                a head's scores are all 0); every-step mode with
+                                STQ_FIT_STEP only */
 } stq_config;
 
 typedef struct stq_layout stq_layout;   /* opaque, host-owned by the library */
@@ -90,7 +96,9 @@ const char *stq_last_error(void);
  * {4,6,8,16,32}, bad enums, comps without window, comps > quantized entries),
  * STQ_ERR_UNSUPPORTED (d_k or d_v not 64/128, window > 16, fp32 units in the
  * windowed mode or on part of a head's key rows, lagged scales with the
- * windowed mode or with key rows of different widths in one head).
+ * windowed mode or with key rows of different widths in one head, row-impact
+ * scores with the windowed mode or lagged scales; a negative or non-finite
+ * score is STQ_ERR_INVALID).
  */
 stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out);
 

@@ -40,7 +40,8 @@ class StqConfig(C.Structure):
     _fields_ = [("H", C.c_int32), ("d_k", C.c_int32), ("d_v", C.c_int32),
                 ("unit", C.c_int32), ("gate", C.c_int32), ("row_scale", C.c_int32),
                 ("col_scale", C.c_int32), ("io_dtype", C.c_int32), ("window", C.c_int32),
-                ("comps", C.c_int32), ("scale_fit", C.c_int32), ("unit_bits", C.POINTER(C.c_uint8))]
+                ("comps", C.c_int32), ("scale_fit", C.c_int32), ("unit_bits", C.POINTER(C.c_uint8)),
+                ("row_impact", C.POINTER(C.c_float))]
 
 
 class StqPool(C.Structure):
@@ -94,10 +95,13 @@ class Layout:
 
     def __init__(self, H, d_k, d_v, unit_bits, *, unit=UNIT_HEAD, gate=GATE_SCALAR,
                  row_scale=F16, col_scale=F16, io_dtype=BF16, window=1, comps=0,
-                 scale_fit=FIT_STEP):
+                 scale_fit=FIT_STEP, row_impact=None):
         self.unit_bits = np.ascontiguousarray(unit_bits, dtype=np.uint8)
+        self.row_impact = None if row_impact is None else np.ascontiguousarray(row_impact, dtype=np.float32)
         self.cfg = StqConfig(H, d_k, d_v, unit, gate, row_scale, col_scale, io_dtype, window,
-                             comps, scale_fit, self.unit_bits.ctypes.data_as(C.POINTER(C.c_uint8)))
+                             comps, scale_fit, self.unit_bits.ctypes.data_as(C.POINTER(C.c_uint8)),
+                             None if self.row_impact is None
+                             else self.row_impact.ctypes.data_as(C.POINTER(C.c_float)))
         h = _P()
         _check(_lib.stq_pack_layout(C.byref(self.cfg), C.byref(h)), "stq_pack_layout")
         self.handle = h
@@ -109,7 +113,7 @@ class Layout:
         self.scale_fit = scale_fit
 
     @classmethod
-    def from_workload(cls, w, unit_bits):
+    def from_workload(cls, w, unit_bits, row_impact=None):
         """Layout of a ``synth.Workload`` (any object with the same fields)."""
         return cls(w.H, w.dk, w.dv, unit_bits,
                    unit=UNIT_KEYROW if w.unit == "keyrow" else UNIT_HEAD,
@@ -118,7 +122,8 @@ class Layout:
                    col_scale=F16 if w.col_scale == "f16" else NONE,
                    io_dtype=BF16 if w.io == "bf16" else F32,
                    window=w.window, comps=w.comps,
-                   scale_fit=FIT_LAGGED if getattr(w, "scale_fit", "step") == "lagged" else FIT_STEP)
+                   scale_fit=FIT_LAGGED if getattr(w, "scale_fit", "step") == "lagged" else FIT_STEP,
+                   row_impact=row_impact)
 
     def head(self, h: int):
         off, nb = C.c_size_t(), C.c_size_t()

@@ -271,6 +271,7 @@ struct Lds {
     float g16[DK];              //   g / 16
     float nog[DK];              //   -2^(w-1) g
     float af[DK];               //   gate
+    float om[DK];               //   row-impact weight (1 without scores)
     float kf[DK], qf[DK];       //   k and q as fp32
     float cf[DV];               // column factor s (the column scale, or 1)
     float isf[DV];              // RN(1 / s)
@@ -435,14 +436,26 @@ __device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir,
 // the state itself (pack, window end).  If emit_o, the column partial sums of
 // o are already in sm.colp and o is combined and stored in the same LDS round
 // as the column maxima.
-template <int DK, int DV, int W, bool SCALED>
+template <int DK, int DV, int W, bool SCALED, bool IMP = false>
 __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd, uint8_t *R,
                                               const Rows &rw, float (&x)[8][8], Lds<DK, DV> &sm,
                                               int t, int rg, int cg, bool emit_o, size_t unit) {
     const bool quant = has_quant<W>(hd);
     const bool cs = quant && A.cs16;
-    // column maxima over quantized rows
-    if (cs) {
+    // column maxima over quantized rows (with row-impact weights: of w_i |x|;
+    // IMP instantiations only, the weighted loop costs registers)
+    if (IMP && cs) {
+        float om[8];
+        lds_read8(&sm.om[8 * rg], om, 0);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (row_w<W>(rw, r) != 16) m = fmaxf(m, om[r] * fabsf(x[r][c]));
+            sm.colm[c][t] = m;
+        }
+    } else if (cs) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             float m = 0.0f;

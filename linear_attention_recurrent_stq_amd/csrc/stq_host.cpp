@@ -10,6 +10,7 @@
 // [K] fp32, delta values [W][d_v] and delta keys [W][d_k] (fp32); for lagged
 // scales (when the head has a quantized row) the next row scales, next column
 // scales, row statistics [d_k] fp32 and column statistics [d_v] fp32.
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -26,7 +27,8 @@ struct stq_layout {
     std::vector<stq::HeadDesc> heads;   // [H]
     std::vector<uint32_t> rows;         // [H*d_k] row table
     std::vector<uint32_t> groups;       // step-kernel head groups (h1 | h2 << 16)
-    std::vector<uint8_t> table;         // device image: heads, rows, groups; 256-B padded
+    std::vector<float> omega;           // row-impact weights [H*d_k] (empty: none)
+    std::vector<uint8_t> table;         // device image: heads, rows, groups, weights; 256-B padded
     size_t slot_bytes = 0;
 };
 
@@ -67,6 +69,17 @@ stq_status check_cfg(const stq_config *c) {
         return fail(STQ_ERR_INVALID, "scale_fit must be STQ_FIT_STEP or STQ_FIT_LAGGED");
     if (c->scale_fit == STQ_FIT_LAGGED && c->window != 1)
         return fail(STQ_ERR_UNSUPPORTED, "lagged scales need the every-step mode (window 1)");
+    if (c->row_impact) {
+        if (c->window != 1 || c->scale_fit != STQ_FIT_STEP)
+            return fail(STQ_ERR_UNSUPPORTED, "row-impact scores need the every-step mode with scales fitted in the step");
+        const size_t nr = (size_t)c->H * (size_t)c->d_k;
+        for (size_t i = 0; i < nr; ++i)
+            if (!(c->row_impact[i] >= 0.0f) || !std::isfinite(c->row_impact[i])) {
+                char m[96];
+                std::snprintf(m, sizeof m, "row_impact[%zu] is negative or not finite", i);
+                return fail(STQ_ERR_INVALID, m);
+            }
+    }
     if (!c->unit_bits) return fail(STQ_ERR_INVALID, "unit_bits is NULL");
     const size_t n = (size_t)c->H * (c->unit == STQ_UNIT_KEYROW ? c->d_k : 1);
     for (size_t i = 0; i < n; ++i) {
@@ -106,6 +119,7 @@ stq::Args base_args(const stq_pool *p, int32_t B, const int32_t *ids) {
     a.rows = reinterpret_cast<const uint32_t *>(base + sizeof(stq::HeadDesc) * L->heads.size());
     a.groups = a.rows + L->rows.size();
     a.ngroups = (int32_t)L->groups.size();
+    a.omega = L->omega.empty() ? nullptr : reinterpret_cast<const float *>(a.groups + L->groups.size());
     a.slot_bytes = L->slot_bytes;
     a.slot_ids = ids;
     a.B = B;
@@ -202,6 +216,7 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
     auto *L = new stq_layout;
     L->cfg = *cfg;
     L->cfg.unit_bits = nullptr;
+    L->cfg.row_impact = nullptr;
     const bool keyrow = cfg->unit == STQ_UNIT_KEYROW;
     const int H = cfg->H, dk = cfg->d_k, dv = cfg->d_v, W = cfg->window, K = cfg->comps;
     L->bits.assign(cfg->unit_bits, cfg->unit_bits + (size_t)H * (keyrow ? dk : 1));
@@ -298,12 +313,26 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
         }
     }
     if (pending >= 0) L->groups.push_back((uint32_t)pending | 0xffff0000u);
+    if (cfg->row_impact) {
+        // w_i = sqrt(score_i / largest score of the head), in double, then fp32
+        L->omega.assign((size_t)H * dk, 1.0f);
+        for (int h = 0; h < H; ++h) {
+            double mx = 0.0;
+            for (int i = 0; i < dk; ++i) mx = std::fmax(mx, (double)cfg->row_impact[(size_t)h * dk + i]);
+            if (mx > 0.0)
+                for (int i = 0; i < dk; ++i)
+                    L->omega[(size_t)h * dk + i] =
+                        (float)std::sqrt((double)cfg->row_impact[(size_t)h * dk + i] / mx);
+        }
+    }
     const size_t hb = sizeof(stq::HeadDesc) * H, rb = sizeof(uint32_t) * (size_t)H * dk;
     const size_t gb = sizeof(uint32_t) * L->groups.size();
-    L->table.assign(up(hb + rb + gb, 256), 0);
+    const size_t ob = sizeof(float) * L->omega.size();
+    L->table.assign(up(hb + rb + gb + ob, 256), 0);
     std::memcpy(L->table.data(), L->heads.data(), hb);
     std::memcpy(L->table.data() + hb, L->rows.data(), rb);
     std::memcpy(L->table.data() + hb + rb, L->groups.data(), gb);
+    if (ob) std::memcpy(L->table.data() + hb + rb + gb, L->omega.data(), ob);
     *out = L;
     return STQ_OK;
 }

@@ -72,6 +72,7 @@ struct Args {
     int32_t lagged;              // STQ_FIT_LAGGED layout
     const uint32_t *groups;      // step kernel: [ngroups] head groups, h1 | h2 << 16
     int32_t ngroups;             //   (h2 = 0xffff: a group of one head)
+    const float *omega;          // row-impact weights [H * d_k] (nullptr: none)
 };
 
 // Launchers (stq_kernels.hip).  Return the launch's hipError_t.  `mixed`: some

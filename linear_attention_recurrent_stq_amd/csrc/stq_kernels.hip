@@ -99,7 +99,8 @@ __device__ __forceinline__ void lag_store(const Args &A, const HeadDesc &hd, uin
 
 // One state.  PRE: a 4-bit state whose inputs were fetched into p (W == 4);
 // otherwise the state's inputs are loaded here.  LAG: a lagged-scale layout.
-template <int DK, int DV, int W, bool PRE, bool LAG = false>
+// IMP: a layout with row-impact weights.
+template <int DK, int DV, int W, bool PRE, bool LAG = false, bool IMP = false>
 __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uint8_t *R, size_t unit,
                                           Lds<DK, DV> &sm, int t, int rg, int cg, const Pre4 &p) {
     static_assert(!PRE || W == 4, "prefetch is for 4-bit heads");
@@ -154,6 +155,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         sm.g16[t] = g * 0.0625f;
         sm.nog[t] = w < 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
         sm.af[t] = in.a;
+        sm.om[t] = A.omega ? A.omega[hd.rows + t] : 1.0f;
         sm.kf[t] = dec_io(in.k, A.io_bf16, t & 1);
         sm.qf[t] = dec_io(in.q, A.io_bf16, t & 1);
     }
@@ -245,7 +247,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         }
     }
     if (LAGQ && fitted) lag_store<DK, DV, LAGQ ? W : 4>(A, hd, R, rw, x, sm, t, rg, cg, unit, in);
-    else requant_store<DK, DV, W, true>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
+    else requant_store<DK, DV, W, true, IMP>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
 }
 
 
@@ -257,7 +259,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 // are all 4-bit rows with FP16 pivot rows (kW4P), 2 if some head mixes other
 // widths; only the per-row paths a layout needs are compiled, which saves
 // registers.
-template <int DK, int DV, int MIX, bool LAG>
+template <int DK, int DV, int MIX, bool LAG, bool IMP = false>
 __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
     constexpr int CG = DV / 8;
     // ngroups == 0: every head alone (small batches keep more workgroups)
@@ -286,31 +288,31 @@ __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
         fetch4<DK, DV, LAG>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
         __builtin_amdgcn_sched_barrier(0);  // keep the first state's loads ahead
         fetch4<DK, DV, LAG>(A, hd2, S + hd2.off, u2, t, rg, cg, p2);
-        step_tile<DK, DV, 4, true, LAG>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
-        step_tile<DK, DV, 4, true, LAG>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
+        step_tile<DK, DV, 4, true, LAG, IMP>(A, hd1, S + hd1.off, u1, sm, t, rg, cg, p1);
+        step_tile<DK, DV, 4, true, LAG, IMP>(A, hd2, S + hd2.off, u2, sm, t, rg, cg, p2);
         return;
     }
     uint8_t *R = S + hd1.off;
     Pre4 none;
     switch (head_width(hd1)) {
-        case 4: step_tile<DK, DV, 4, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 6: step_tile<DK, DV, 6, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 8: step_tile<DK, DV, 8, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 16: step_tile<DK, DV, 16, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
-        case 32: step_tile<DK, DV, 32, false, LAG>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 4: step_tile<DK, DV, 4, false, LAG, IMP>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 6: step_tile<DK, DV, 6, false, LAG, IMP>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 8: step_tile<DK, DV, 8, false, LAG, IMP>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 16: step_tile<DK, DV, 16, false, LAG, IMP>(A, hd1, R, u1, sm, t, rg, cg, none); break;
+        case 32: step_tile<DK, DV, 32, false, LAG, IMP>(A, hd1, R, u1, sm, t, rg, cg, none); break;
         case kW4P:
-            if (MIX >= 1) step_tile<DK, DV, kW4P, false>(A, hd1, R, u1, sm, t, rg, cg, none);
+            if (MIX >= 1) step_tile<DK, DV, kW4P, false, false, IMP>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
         default:
-            if (MIX == 2) step_tile<DK, DV, 0, false>(A, hd1, R, u1, sm, t, rg, cg, none);
+            if (MIX == 2) step_tile<DK, DV, 0, false, false, IMP>(A, hd1, R, u1, sm, t, rg, cg, none);
             break;
     }
 }
 
-template <int DK, int DV, int MIX>
+template <int DK, int DV, int MIX, bool IMP = false>
 __global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
     __shared__ Lds<DK, DV> sm;
-    step_groups<DK, DV, MIX, false>(A, sm);
+    step_groups<DK, DV, MIX, false, IMP>(A, sm);
 }
 
 // Lagged scales (heads of one width, MIX 0): held to 4 waves per SIMD, the
@@ -329,6 +331,9 @@ __device__ __forceinline__ void pack_tile(const Args &A, const HeadDesc &hd, uin
                                           Lds<DK, DV> &sm, int t, int rg, int cg, size_t unit) {
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
+    // row-impact weights for the column maxima (1 without scores)
+    if (t < DK) sm.om[t] = A.omega ? A.omega[hd.rows + t] : 1.0f;
+    __syncthreads();
     float x[8][8];
     const float *src = A.state + unit * DK * DV;
 #pragma unroll
@@ -338,7 +343,7 @@ __device__ __forceinline__ void pack_tile(const Args &A, const HeadDesc &hd, uin
         x[r][0] = a.x; x[r][1] = a.y; x[r][2] = a.z; x[r][3] = a.w;
         x[r][4] = b.x; x[r][5] = b.y; x[r][6] = b.z; x[r][7] = b.w;
     }
-    requant_store<DK, DV, W, false>(A, hd, R, rw, x, sm, t, rg, cg, false, unit);
+    requant_store<DK, DV, W, false, true>(A, hd, R, rw, x, sm, t, rg, cg, false, unit);
     if (A.lagged && has_quant<W>(hd)) {
         // no next scales yet: the next step refits in the step
         if (t < DK) {
@@ -501,7 +506,8 @@ hipError_t launch_step_dims(Args a, hipStream_t s) {
     if (a.B == 0) return hipSuccess;
     if ((size_t)a.B * a.H < kPairMinStates) a.ngroups = 0;
     const size_t per_request = a.ngroups ? (size_t)a.ngroups : (size_t)a.H;
-    void (*k)(Args) = k_step<DK, DV, MIX>;
+    // layouts with row-impact weights take the instantiation that weighs
+    void (*k)(Args) = a.omega ? k_step<DK, DV, MIX, true> : k_step<DK, DV, MIX, false>;
     hipLaunchKernelGGL(k, dim3((unsigned)((size_t)a.B * per_request)), dim3(DK * DV / 64), 0, s, a);
     return hipGetLastError();
 }

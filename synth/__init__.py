@@ -30,7 +30,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # tensor ids of the stream keys
-T_Q, T_K, T_V, T_GATE, T_BETA, T_INIT, T_LAYOUT, T_GATE_OFFSET = 1, 2, 3, 4, 5, 6, 7, 8
+T_Q, T_K, T_V, T_GATE, T_BETA, T_INIT, T_LAYOUT, T_GATE_OFFSET, T_Q_SCALE = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 def _mix(z: np.ndarray) -> np.ndarray:
@@ -107,6 +107,8 @@ class Workload:
     desc: str = ""
     scale_fit: str = "step"  # "step" (refit inside each step) | "lagged" (fitted apart)
     gate_spread: float = 0.0  # KDA: per key row fixed offset U(-spread, spread) of the gate's N(2, 1)
+    query_spread: float = 0.0  # per key channel fixed query scale exp(spread N(0,1)) before normalizing
+    impact: str = "none"       # "none" | "queries": row-impact scores E[q_i^2] from calibration queries
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -154,6 +156,12 @@ WORKLOADS = {
         desc="KDA B=256 H=32 d=128 T=256, key rows of different lifetimes (fixed per-row "
              "gate offsets), widths from a calibration pass and the lifetime-aware allocation "
              "(mean 6 bits, 1% pivot rows)"),
+    "kimi_impact": Workload(
+        "kimi_impact", 11, B=256, H=32, dk=128, dv=128, T=256, unit="keyrow", gate="keyvec",
+        row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.01,
+        init="outlier", query_spread=1.0, impact="queries",
+        desc="the KDA layer with queries of unequal weight per key channel and row-impact "
+             "scores E[q_i^2] from calibration queries (impact-weighted column scales)"),
     "windowed_kda": Workload(
         "windowed_kda", 5, B=512, H=32, dk=128, dv=128, T=1024, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="uniform8", pivot_frac=0.0,
@@ -240,6 +248,8 @@ def step_inputs(w: Workload, layer: int, t: int, b, h) -> StepInputs:
     b, h = np.broadcast_arrays(b, h)
     key = lambda tensor: stream_key(w.seed, w.cid, tensor, layer, t, b, h)
     q = normal(key(T_Q), w.dk)
+    if w.query_spread:
+        q = q * query_scales(w, layer, h)
     k = normal(key(T_K), w.dk)
     v = normal(key(T_V), w.dv)
     q = q / np.linalg.norm(q, axis=-1, keepdims=True)
@@ -257,6 +267,14 @@ def step_inputs(w: Workload, layer: int, t: int, b, h) -> StepInputs:
         return StepInputs(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
                           a, beta, qb, kb, vb)
     return StepInputs(q32, k32, v32, a, beta)
+
+
+def query_scales(w: Workload, layer: int, h) -> np.ndarray:
+    """Fixed per-key-channel query scale exp(spread * N(0,1)), one per
+    (layer, head, channel), applied before the query is normalized: some key
+    rows are read far more than others.  [..., d_k]"""
+    h = np.asarray(h, dtype=np.int64)
+    return np.exp(w.query_spread * normal(stream_key(w.seed, w.cid, T_Q_SCALE, layer, 0, h), w.dk))
 
 
 def gate_offsets(w: Workload, layer: int, h) -> np.ndarray:

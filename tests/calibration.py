@@ -48,3 +48,14 @@ def allocated_bits(w: synth.Workload, layer: int = 0, B: int = 8, steps: int = 4
     n = g.size
     pivots = max(1, int(round(w.pivot_frac * n))) if w.pivot_frac > 0 else 0
     return np.array(allocator.allocate(g.tolist(), m.tolist(), avg_bits, pivots), np.uint8), g, m
+
+
+def query_impact(w: synth.Workload, layer: int, B: int, steps: int) -> np.ndarray:
+    """Row-impact scores iota_i = E[q_i^2] per (head, key row) from the
+    calibration queries (the first B requests, `steps` steps), float32 [H*d_k]:
+    an error in row i of the state reaches the output through q_i."""
+    acc = np.zeros((w.H, w.dk))
+    for t in range(steps):
+        x = synth.step_inputs(w, layer, t, np.arange(B)[:, None], np.arange(w.H)[None, :])
+        acc += (x.q.astype(np.float64) ** 2).sum(axis=0)
+    return (acc / (B * steps)).reshape(-1).astype(np.float32)

@@ -21,14 +21,14 @@ THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 class Harness:
     def __init__(self, w: synth.Workload, layer: int = 0, follow=None, seed_perm: int = 1,
-                 bits=None):
+                 bits=None, row_impact=None):
         import torch
         import linear_attention_recurrent_stq_amd as stq
         self.torch, self.stq = torch, stq
         self.w, self.layer = w, layer
         self.bits = synth.unit_bits(w, layer) if bits is None else np.asarray(bits, np.uint8)
-        self.L = stq.Layout.from_workload(w, self.bits)
-        self.ocfg = oracle.Cfg.from_workload(w, self.bits)
+        self.L = stq.Layout.from_workload(w, self.bits, row_impact=row_impact)
+        self.ocfg = oracle.Cfg.from_workload(w, self.bits, row_impact=row_impact)
         assert self.L.slot_bytes == self.ocfg.slot_bytes
         self.pool = stq.Pool(self.L, w.B)
         # requests are mapped to a seeded permutation of the slots

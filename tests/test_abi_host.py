@@ -243,3 +243,26 @@ def test_lagged_layout_matches_oracle(stq, ora):
         assert L.slot_bytes == o.slot_bytes
         for h in range(5):
             assert L.head(h) == (o.head_layout(h)["base"], o.head_layout(h)["bytes"])
+
+
+def test_row_impact_validation(stq):
+    """Row-impact scores: negative or non-finite scores are rejected; the
+    windowed mode and lagged scales take none; the weights add H*d_k floats
+    to the pool's table header."""
+    bits = np.full(4, 4, np.uint8)
+    good = np.ones(4 * 128, np.float32)
+    plain = stq.Layout(4, 128, 128, bits)
+    L = stq.Layout(4, 128, 128, bits, row_impact=good)
+    assert L.slot_bytes == plain.slot_bytes
+    groups = 2  # four 4-bit heads in two pairs
+    assert plain.header_bytes == (64 * 4 + 4 * 4 * 128 + 4 * groups + 255) // 256 * 256
+    assert L.header_bytes == (64 * 4 + 4 * 4 * 128 + 4 * groups + 4 * 4 * 128 + 255) // 256 * 256
+    for bad in (-1.0, np.nan, np.inf):
+        b = good.copy()
+        b[17] = bad
+        with pytest.raises(stq.StqError, match="row_impact"):
+            stq.Layout(4, 128, 128, bits, row_impact=b)
+    with pytest.raises(stq.StqError, match="row-impact"):
+        stq.Layout(4, 128, 128, np.full(4, 8, np.uint8), window=4, row_impact=good)
+    with pytest.raises(stq.StqError, match="row-impact"):
+        stq.Layout(4, 128, 128, bits, scale_fit=stq.FIT_LAGGED, row_impact=good)

@@ -33,9 +33,9 @@ def _check_step(o_gpu, o_ref, follow, t, tag):
     return 0.0
 
 
-def _run(w, T, follow=None, bits=None, check_slots_every=0, tag=""):
+def _run(w, T, follow=None, bits=None, check_slots_every=0, tag="", row_impact=None):
     print(f"[{tag}] {w.name} B={w.B} H={w.H} d={w.dk} T={T}", flush=True)
-    hs = _harness(w, follow=follow, bits=bits)
+    hs = _harness(w, follow=follow, bits=bits, row_impact=row_impact)
     try:
         hs.init_state()
         if w.init != "zero":
@@ -101,7 +101,8 @@ def test_allocated_row_widths_d128():
     _run(w, 12, bits=bits, check_slots_every=4, tag="kda-allocated")
 
 
-def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None, bits=None):
+def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None, bits=None,
+                 row_impact=None):
     """Full batch on the GPU; n_units seeded (request, head) units (or the
     given list) followed by the oracle over T steps (the others keep their
     first inputs)."""
@@ -113,7 +114,7 @@ def _run_sampled(w, T, n_units, seed, layer=0, track=False, tag="", follow=None,
     follow = sorted(follow)
     print(f"[{tag}] {w.name} layer {layer}: {len(follow)} followed units of B={w.B} x H={w.H}, "
           f"T={T}", flush=True)
-    hs = _harness(w, layer=layer, follow=follow, bits=bits)
+    hs = _harness(w, layer=layer, follow=follow, bits=bits, row_impact=row_impact)
     try:
         if track:
             hs.track_fp32()
@@ -661,3 +662,23 @@ def test_calibration_matches_oracle_and_allocated_widths_step_exactly():
     assert np.median(lt[bits == 8]) > np.median(lt[bits == 4])
     print(f"[allocated] widths {dict(zip(*np.unique(bits, return_counts=True)))}", flush=True)
     _run(w.with_(B=8), 24, bits=bits, check_slots_every=8, tag="allocated")
+
+
+# ------------------------------------------------------------ row impact
+
+def test_row_impact_weighted_fit():
+    """Row-impact-weighted column scales (scores E[q_i^2] from calibration
+    queries on the KDA layer whose queries weigh key channels unequally):
+    every unit of 4 requests over 24 steps from the outlier start, slot bytes
+    compared every 4 steps (4-bit rows with FP16 pivot rows); every unit of a
+    6-bit GDN layer with the same scores per head; and the full 256 x 32
+    batch with 64 followed units over 64 steps."""
+    from tests.calibration import query_impact
+    w = synth.WORKLOADS["kimi_impact"]
+    iota = query_impact(w, 0, 16, 16)
+    assert iota.max() > 20 * iota.min()   # the scores do differ
+    _run(w.with_(B=4), 24, check_slots_every=4, tag="impact", row_impact=iota)
+    g = synth.WORKLOADS["qwen_gdn"].with_(B=4, bits="uniform6", init="outlier", query_spread=1.0,
+                                          name="qwen_impact")
+    _run(g, 16, check_slots_every=4, tag="impact-gdn", row_impact=iota)
+    _run_sampled(w, 64, 64, seed=61, tag="impact-full", row_impact=iota)
