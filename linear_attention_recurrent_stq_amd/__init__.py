@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libstq.so")
+# STQ_LIBRARY selects another build of this library (libstq_debug.so,
+# libstq_san.so); the default is the release build next to this file
+LIB_PATH = os.environ.get("STQ_LIBRARY") or os.path.join(HERE, "libstq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

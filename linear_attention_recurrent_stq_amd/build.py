@@ -5,6 +5,11 @@ Each source is compiled to an object of its own (in parallel, under
 kernels are also linked with the host source built with STQ_DEBUG_VALIDATE
 into ``libstq_debug.so``: there every call that takes slot ids copies them to
 the host and rejects duplicates and out-of-range ids before any launch.
+
+``build_sanitized()`` links the same kernels with the host sources built with
+AddressSanitizer and UndefinedBehaviorSanitizer (host code only; the device
+code is the release code) into ``libstq_san.so``, for the CPU test suite run
+by ``tests/sanitize.sh``.
 """
 from __future__ import annotations
 
@@ -17,6 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libstq.so")
 LIB_DEBUG = os.path.join(HERE, "libstq_debug.so")
+LIB_SAN = os.path.join(HERE, "libstq_san.so")
+# host-only sanitizer flags (each -fsanitize= behind -Xarch_host: no GPU code is built with it)
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+       "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 OBJDIR = os.path.join(ROOT, "_build")
 SOURCES = [os.path.join(HERE, "csrc", f)
            for f in ("stq_host.cpp", "stq_alloc.cpp", "stq_kernels.hip", "stq_window.hip")]
@@ -77,6 +86,35 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(verbose: bool = False) -> str:
+    """libstq_san.so: host sources with ASan + UBSan, kernels as in the release
+    build (build() must have run).  Load it with clang's shared ASan runtime
+    preloaded (tests/sanitize.sh)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs = []
+    for src in SOURCES:
+        if src.endswith(".hip"):
+            objs.append(os.path.join(OBJDIR, os.path.basename(src) + ".o"))
+            continue
+        obj = os.path.join(OBJDIR, "san_" + os.path.basename(src) + ".o")
+        cmd = [HIPCC, *FLAGS, "-O1", *SAN, *inc, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        objs.append(obj)
+    tmp = LIB_SAN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-shared-libasan", *SAN, *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB_SAN)
+    return LIB_SAN
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB, LIB_DEBUG)
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        build(verbose="-v" in sys.argv)
+        print(LIB, LIB_DEBUG)

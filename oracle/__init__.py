@@ -17,18 +17,33 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "stq_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+LIB_SAN = os.path.join(HERE, "liboracle_san.so")
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
           "-Wall", "-Wextra"]
+SANFLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+            "-shared-libasan"]
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no contraction of a*b+c into fma, no fast math)."""
+    if os.environ.get("ORACLE_LIBRARY"):
+        return os.environ["ORACLE_LIBRARY"]   # a prebuilt build (the sanitizer run)
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"])
         os.replace(tmp, LIB)
     return LIB
+
+
+def build_sanitized() -> str:
+    """The oracle with AddressSanitizer + UndefinedBehaviorSanitizer, built with
+    clang so that it shares clang's ASan runtime with the library's sanitizer
+    build (tests/sanitize.sh)."""
+    tmp = LIB_SAN + ".tmp%d" % os.getpid()
+    subprocess.check_call(["/opt/rocm/llvm/bin/clang", *CFLAGS, *SANFLAGS, SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, LIB_SAN)
+    return LIB_SAN
 
 
 class _Cfg(C.Structure):
@@ -45,8 +60,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(LIB)
+        L = C.CDLL(build())
         P = C.c_void_p
         L.ora_slot_bytes.restype = C.c_size_t
         L.ora_slot_bytes.argtypes = [P]

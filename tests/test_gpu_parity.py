@@ -682,3 +682,66 @@ def test_row_impact_weighted_fit():
                                           name="qwen_impact")
     _run(g, 16, check_slots_every=4, tag="impact-gdn", row_impact=iota)
     _run_sampled(w, 64, 64, seed=61, tag="impact-full", row_impact=iota)
+
+
+# ------------------------------------------------------------ snapshot / resume
+
+@pytest.mark.parametrize("name,T", [("qwen_gdn", 24), ("windowed_kda", 40), ("serving_lagged", 24)])
+def test_snapshot_and_resume(name, T):
+    """A slot is the whole state of a request: stepping T steps straight
+    through equals stepping T/2, copying the slots' bytes into a fresh pool at
+    other slot positions, and stepping T/2 more there (outputs and final
+    bytes identical).  Every-step layout; windowed layout resumed in the
+    middle of a window; lagged scales (next scales and statistics travel with
+    the slot)."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS[name].with_(B=6, layers=1)
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    lagged = getattr(w, "scale_fit", "step") == "lagged"
+    io = torch.bfloat16 if w.io == "bf16" else torch.float32
+
+    def inputs(t):
+        x = synth.batch_inputs(w, 0, t)
+        cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+        return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits), torch.from_numpy(x.a).cuda(), \
+            torch.from_numpy(x.beta).cuda()
+
+    def run(pool, ids, t0, t1, outs):
+        o = torch.empty(w.B, w.H, w.dv, device="cuda")
+        for t in range(t0, t1):
+            stq.decode_step(pool, ids, *inputs(t), o)
+            if lagged:
+                stq.fit_scales(pool, ids)
+            outs.append(o.cpu().numpy().copy())
+
+    def seed(pool, ids):
+        if w.init != "zero":
+            bb, hh = np.meshgrid(np.arange(w.B), np.arange(w.H), indexing="ij")
+            stq.pack(pool, ids, torch.from_numpy(synth.initial_state(w, 0, bb, hh)).cuda())
+
+    ids_a = torch.arange(w.B, dtype=torch.int32, device="cuda")
+    straight = stq.Pool(L, w.B)
+    seed(straight, ids_a)
+    out_a = []
+    run(straight, ids_a, 0, T, out_a)
+
+    first = stq.Pool(L, w.B)
+    seed(first, ids_a)
+    out_b = []
+    run(first, ids_a, 0, T // 2, out_b)
+    snap = first.slots_view().cpu()                      # request b lives in slot b
+    second = stq.Pool(L, w.B + 3)                        # a larger pool, other positions
+    where = np.array([7, 0, 4, 2, 8, 5], np.int32)[:w.B]
+    view = second.slots_view()
+    for b in range(w.B):
+        view[int(where[b])].copy_(snap[b].cuda())
+    ids_c = torch.from_numpy(where).cuda()
+    run(second, ids_c, T // 2, T, out_b)
+    torch.cuda.synchronize()
+    for t in range(T):
+        assert np.array_equal(out_a[t], out_b[t]), (name, t)
+    fa, fc = straight.slots_view().cpu().numpy(), second.slots_view().cpu().numpy()
+    for b in range(w.B):
+        assert np.array_equal(fa[b], fc[int(where[b])]), (name, b)
