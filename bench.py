@@ -104,10 +104,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
+def step_kernel(w: synth.Workload) -> str:
+    """Name of the kernel a stq_decode_step call of this workload spends its time in."""
+    if w.window > 1:
+        return "k_win"
+    return "k_step_lag" if w.scale_fit == "lagged" else "k_step"
+
+
+def counter_traffic(w: synth.Workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"k_step_{workload}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{step_kernel(w)}_{w.name}_counters.txt")
     try:
         kv = dict(line.split(":", 1) for line in open(path) if ":" in line and not line.startswith("#"))
     except OSError:
@@ -379,8 +386,8 @@ def main() -> int:
                       "p90": round(float(np.percentile(launch_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic(w.name),
-                     "kernel": "k_win + k_win_end" if w.window > 1 else "k_step",
+                     "traffic": counter_traffic(w),
+                     "kernel": "k_win + k_win_end" if w.window > 1 else step_kernel(w),
                      "bytes_per_launch": int(per_launch_bytes)},
         "wall_s": round(wall, 3),
     }

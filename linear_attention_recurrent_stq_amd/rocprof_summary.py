@@ -12,8 +12,9 @@
       SQ_WAVES pass, and VALU issues per state element (x 64 lanes / elements)
 
 CMD is the command line that produced DIR (recorded in the summary).  The
-decode kernels are k_step (every-step mode) and k_win + k_win_end (windowed:
-one stq_decode_step call launches both).
+decode kernels are k_step (every-step mode), k_step_lag (lagged scales; the
+fit of the next scales, k_fit, is a separate call and not counted) and k_win +
+k_win_end (windowed: one stq_decode_step call launches both).
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-STEP_KERNELS = ("::k_step<", "::k_win<", "::k_win_end<")
+STEP_KERNELS = ("::k_step<", "::k_step_lag<", "::k_win<", "::k_win_end<")
 COPY_KERNEL = "copyBuffer"
 
 
