@@ -435,11 +435,14 @@ __device__ __forceinline__ void quant_row(uint8_t *row, int cg, int w, float ir,
 // of the column factor s in sm.cf (the step's working state); otherwise x is
 // the state itself (pack, window end).  If emit_o, the column partial sums of
 // o are already in sm.colp and o is combined and stored in the same LDS round
-// as the column maxima.
+// as the column maxima.  fw (kW4P heads, uniform over the wave): no block of
+// the wave holds a pivot row, so every row is 4-bit and rows follow each
+// other at d_v/2 bytes from rw.base.
 template <int DK, int DV, int W, bool SCALED, bool IMP = false>
 __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd, uint8_t *R,
                                               const Rows &rw, float (&x)[8][8], Lds<DK, DV> &sm,
-                                              int t, int rg, int cg, bool emit_o, size_t unit) {
+                                              int t, int rg, int cg, bool emit_o, size_t unit,
+                                              bool fw = false) {
     const bool quant = has_quant<W>(hd);
     const bool cs = quant && A.cs16;
     // column maxima over quantized rows (with row-impact weights: of w_i |x|;
@@ -453,6 +456,15 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 if (row_w<W>(rw, r) != 16) m = fmaxf(m, om[r] * fabsf(x[r][c]));
+            sm.colm[c][t] = m;
+        }
+    } else if (cs && (!per_row<W>() || fw)) {
+        // every row quantized: two elements per max3
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float m = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) m = fmaxf(m, fabsf(x[r][c]));
             sm.colm[c][t] = m;
         }
     } else if (cs) {
@@ -510,7 +522,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         float m = 0.0f;
-        if (row_w<W>(rw, r) != 16) {
+        if (fw || row_w<W>(rw, r) != 16) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const float z = x[r][c] * icc[c];
@@ -550,16 +562,21 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
     for (int c = 0; c < 8; ++c) scc[c] = 1.0f;
     if (SCALED && per_row<W>()) lds_read8(&sm.cf[8 * cg], scc, 0);
-    bool anysat = false;
+    // a negative 1/r' marks a saturated row; the minimum finds one in three
+    // min3 operations (a flag per row costs a compare and a select each)
+    float irmin = irr[0];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) anysat |= irr[r] < 0.0f;
-    if (__builtin_expect(__any(anysat), 0)) {
+    for (int r = 1; r < 8; ++r) irmin = fminf(irmin, irr[r]);
+    if (__builtin_expect(__any(irmin < 0.0f), 0)) {
         // a row step saturated at 65504: clamp codes to +-qmax
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             if (row_w<W>(rw, r) == 16) store_piece(R + row_o<DV, W>(rw, r), cg, 16, pivot_piece_s<SCALED>(x[r], scc));
             else quant_row<true>(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r), fabsf(irr[r]), x[r]);
         }
+    } else if (W == kW4P && fw) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) quant_row<false>(R + rw.base + (uint32_t)r * (DV / 2), cg, 4, irr[r], x[r]);
     } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {

@@ -108,6 +108,9 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     const bool quant = has_quant<W>(hd);
     Rows rw;
     row_geometry<DV, W>(A, hd, rg, rw);
+    // kW4P heads: no block of this wave holds a pivot row (uniform over the
+    // wave; most waves, as pivot rows are few), so the wave runs the 4-bit code
+    const bool fw = W == kW4P && !__any(rw.m8 != 0u);
     uint4 raw[8];
     uint4 pv = make_uint4(0, 0, 0, 0);  // kW4P: the piece of the thread's first pivot row
     int pr = -1;                        //      and that row
@@ -124,6 +127,10 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     } else if (PRE) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) raw[r] = make_uint4(p.raw[r], 0, 0, 0);
+    } else if (W == kW4P && fw) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            raw[r] = make_uint4(*reinterpret_cast<const uint32_t *>(R + rw.base + (uint32_t)r * (DV / 2) + 4 * cg), 0, 0, 0);
     } else if (W == kW4P) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -180,7 +187,19 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     // partial sums over the thread's 8 rows accumulated as the rows come in.
     // Vectors are read from LDS where they are used, so that none of them is
     // held across a barrier.
-    {
+    if (W == kW4P && fw) {
+        float kk[8], s[8];
+        lds_read8(&sm.kf[8 * rg], kk, 0);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int i = 8 * rg + r;
+            dequant_row(raw[r], 4, sm.g[i], sm.g16[i], sm.nog[i], x[r]);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s[c] = r == 0 ? x[0][c] * kk[0] : fma_(x[r][c], kk[r], s[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sm.colp[c][t] = s[c];
+    } else {
         float kk[8], s[8];
         lds_read8(&sm.kf[8 * rg], kk, 0);
 #pragma unroll
@@ -247,7 +266,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         }
     }
     if (LAGQ && fitted) lag_store<DK, DV, LAGQ ? W : 4>(A, hd, R, rw, x, sm, t, rg, cg, unit, in);
-    else requant_store<DK, DV, W, true, IMP>(A, hd, R, rw, x, sm, t, rg, cg, true, unit);
+    else requant_store<DK, DV, W, true, IMP>(A, hd, R, rw, x, sm, t, rg, cg, true, unit, fw);
 }
 
 

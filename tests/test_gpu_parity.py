@@ -322,6 +322,62 @@ def test_unpack_and_pack_match_oracle():
         hs.close()
 
 
+def _saturated_rows(hs) -> int:
+    """Quantized rows of the followed units (oracle side) whose fp16 row scale
+    is 65504, the largest fp16."""
+    n = 0
+    for b, h in hs.follow:
+        lay = hs.ocfg.head_layout(h)
+        if lay["nquant"] == 0:
+            continue
+        lo = lay["base"] + lay["rs"]
+        n += int((hs.oslots[b][lo:lo + 2 * hs.w.dk].view(np.uint16) == 0x7BFF).sum())
+    return n
+
+
+@pytest.mark.parametrize("name", ["serving_gdn", "qwen_gdn", "kimi_kda"])
+def test_saturated_rows_clamp_codes(name):
+    """Rows beyond the fp16 range: a packed state with rows of ~1e11 and steps
+    whose v are scaled by 2^40 push row scales to 65504, where codes are
+    clamped to +-qmax.  Every unit's slot bytes after pack and after every
+    step, and every output, equal the oracle's (4-bit pairs and a pivot head;
+    4/6/8-bit heads; 4-bit rows with FP16 pivot rows)."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS[name].with_(B=4, layers=1)
+    print(f"[saturated] {w.name} B={w.B}", flush=True)
+    hs = _harness(w)
+    try:
+        rng = np.random.default_rng(7)
+        M = (rng.standard_normal((w.B, w.H, w.dk, w.dv)) * 0.3).astype(np.float32)
+        big = np.float32(2.0 ** 40)
+        M[:, :, 3] *= big
+        M[:, :, 77] *= big
+        stq.pack(hs.pool, hs.slot_ids, torch.from_numpy(M).cuda())
+        for b, h in hs.follow:
+            hs.ocfg.pack_head(hs.oslots[b], h, M[b, h])
+        assert not hs.compare_slots()
+        assert _saturated_rows(hs) > 0
+        sat_steps = 0
+        for t in range(6):
+            x = hs.load_full(t)
+            if t in (1, 3):
+                # v of requests 0 and 2 times 2^40 (exact: a power of two)
+                x.v[[0, 2]] *= big
+                if x.v_bits is not None:
+                    x.v_bits[[0, 2]] = (x.v[[0, 2]].view(np.uint32) >> 16).astype(np.uint16)
+                _, _, v = hs._to_dev(x)
+                hs.v.copy_(v)
+            o_gpu, o_ref = hs.step(x)
+            _check_step(o_gpu, o_ref, hs.follow, t, "saturated")
+            bad = hs.compare_slots()
+            assert not bad, f"slot bytes differ after step {t}: {bad[:4]}"
+            sat_steps += _saturated_rows(hs) > 0
+        assert sat_steps >= 2
+    finally:
+        hs.close()
+
+
 def test_invalid_slot_id_touches_nothing():
     """An out-of-range slot id yields a NaN output and leaves every slot unchanged."""
     import torch
