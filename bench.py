@@ -88,6 +88,8 @@ def launch_bytes(w: synth.Workload, bits: np.ndarray) -> float:
     return w.B * (state + state / W + w.H * per_head / W + io)
 
 
+INIT_REQUESTS = 32  # requests whose outlier initial states are drawn (then repeated)
+
 # the sources the device code is compiled from (host-only files excluded)
 DEVICE_SOURCES = ("stq_device.h", "stq_internal.h", "stq_kernels.hip", "stq_window.hip")
 
@@ -271,9 +273,16 @@ def main() -> int:
         as_.append(torch.from_numpy(x.a).to(dev)); bs.append(torch.from_numpy(x.beta).to(dev))
     o = torch.empty(w.B, w.H, w.dv, dtype=torch.float32, device=dev)
     if w.init != "zero":
-        bb, hh = np.meshgrid(np.arange(w.B), np.arange(w.H), indexing="ij")
+        # seeded outlier states of the first INIT_REQUESTS requests, repeated
+        # over the batch: drawing every state of a large pool on the host
+        # takes minutes, and the values do not change the cost of a step
+        n0 = min(w.B, INIT_REQUESTS)
+        bb, hh = np.meshgrid(np.arange(n0), np.arange(w.H), indexing="ij")
         for l, (L, pool, _) in enumerate(layers):
-            stq.pack(pool, ids, torch.from_numpy(synth.initial_state(w, l, bb, hh)).to(dev))
+            m0 = torch.from_numpy(synth.initial_state(w, l, bb, hh)).to(dev)
+            reps = (w.B + n0 - 1) // n0
+            stq.pack(pool, ids, m0.repeat(reps, 1, 1, 1)[: w.B].contiguous())
+            del m0
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()

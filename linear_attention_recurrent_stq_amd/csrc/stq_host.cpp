@@ -300,11 +300,13 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
     L->slot_bytes = slot;
     // Head groups of the step kernel: 4-bit heads in pairs (one workgroup
     // steps both, fetching the second while computing the first), every
-    // other head alone.
+    // other head alone.  The pairs come first: the grid runs group-major, so
+    // a launch ends with the single heads, its shortest workgroups.
+    std::vector<uint32_t> singles;
     int pending = -1;
     for (int h = 0; h < H; ++h) {
         if (L->heads[h].width != 4) {
-            L->groups.push_back((uint32_t)h | 0xffff0000u);
+            singles.push_back((uint32_t)h | 0xffff0000u);
         } else if (pending < 0) {
             pending = h;
         } else {
@@ -312,7 +314,8 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
             pending = -1;
         }
     }
-    if (pending >= 0) L->groups.push_back((uint32_t)pending | 0xffff0000u);
+    if (pending >= 0) singles.push_back((uint32_t)pending | 0xffff0000u);
+    L->groups.insert(L->groups.end(), singles.begin(), singles.end());
     if (cfg->row_impact) {
         // w_i = sqrt(score_i / largest score of the head), in double, then fp32
         L->omega.assign((size_t)H * dk, 1.0f);

@@ -281,10 +281,18 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
 template <int DK, int DV, int MIX, bool LAG, bool IMP = false>
 __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
     constexpr int CG = DV / 8;
-    // ngroups == 0: every head alone (small batches keep more workgroups)
-    const int ng = A.ngroups ? A.ngroups : A.H;
-    const int b = (int)(blockIdx.x / (uint32_t)ng);
-    const int gi = (int)(blockIdx.x - (uint32_t)b * ng);
+    // ngroups == 0: every head alone (small batches keep more workgroups),
+    // request-major.  With groups the grid is group-major: the pairs, which
+    // the group table lists first, of every request, then the heads stepped
+    // alone, so the launch ends with its shortest workgroups
+    int b, gi;
+    if (A.ngroups) {
+        gi = (int)(blockIdx.x / (uint32_t)A.B);
+        b = (int)(blockIdx.x - (uint32_t)gi * (uint32_t)A.B);
+    } else {
+        b = (int)(blockIdx.x / (uint32_t)A.H);
+        gi = (int)(blockIdx.x - (uint32_t)b * (uint32_t)A.H);
+    }
     const uint32_t grp = A.ngroups ? A.groups[gi] : ((uint32_t)gi | 0xffff0000u);
     const int h1 = (int)(grp & 0xffffu), h2 = (int)(grp >> 16);
     const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;

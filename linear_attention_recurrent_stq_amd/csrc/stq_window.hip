@@ -44,8 +44,10 @@ struct LdsW {
         };
         struct {
             uint32_t cix[kKMax];      // compensation index p (old entries; later the candidate list)
-            float cvl[kKMax];         // compensation value
+            float cvl[kKMax];         // compensation value (during a selection: the histogram,
+                                      // then the chosen entries)
             uint32_t ckey[kCandMax];  // candidate keys
+            float csv[kCandMax];      // candidate values
         };
     };
     uint32_t cstart[DV + 1];  // old entries of column j: cstart[j] .. cstart[j+1]-1
@@ -132,6 +134,75 @@ __device__ __forceinline__ bool chosen(float v, uint32_t p, float thr, uint32_t 
     return (v > thr) || (v == thr && p <= pk);
 }
 
+// Radix selection with LDS histograms of 256 bins (8-bit digits).  A pass
+// histograms one digit of the keys that match the digits found so far; one
+// wave then scans the bins (lane l owns bins 4l .. 4l+3) and broadcasts the
+// digit through bc.
+
+// Bits above digit `shift` (the digits already found).
+__device__ __forceinline__ uint32_t above_digit(int shift) { return shift >= 24 ? 0u : ~0u << (shift + 8); }
+
+// Largest digit d with (count of bins >= d) >= need: bc[0] = d, bc[1] = the
+// count in bins above d, bc[2] = the count in bin d.  need >= 1 and the
+// histogram holds at least need keys.
+__device__ __forceinline__ void find_desc(const uint32_t *hist, uint32_t need, uint32_t *bc, int t) {
+    if (t >= 64) return;
+    const uint4 h = reinterpret_cast<const uint4 *>(hist)[t];
+    const uint32_t local = h.x + h.y + h.z + h.w;
+    uint32_t S = local;  // keys in the bins of lanes >= t
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(S, off, 64);
+        if (t + off < 64) S += o;
+    }
+    const uint32_t s3 = S - local + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
+    int d = -1;
+    uint32_t above = 0, eq = 0;
+    if (s3 >= need) { d = 4 * t + 3; above = s3 - h.w; eq = h.w; }
+    else if (s2 >= need) { d = 4 * t + 2; above = s2 - h.z; eq = h.z; }
+    else if (s1 >= need) { d = 4 * t + 1; above = s1 - h.y; eq = h.y; }
+    else if (s0 >= need) { d = 4 * t; above = s0 - h.x; eq = h.x; }
+    // suffix counts fall with the lane, so the lanes holding a digit are 0 .. L
+    const unsigned long long m = __ballot(d >= 0);
+    if (t == 63 - __clzll(m)) {
+        bc[0] = (uint32_t)d;
+        bc[1] = above;
+        bc[2] = eq;
+    }
+}
+
+// Smallest digit d with (count of bins <= d) >= need: bc[0] = d, bc[1] = the
+// count in bins below d.
+__device__ __forceinline__ void find_asc(const uint32_t *hist, uint32_t need, uint32_t *bc, int t) {
+    if (t >= 64) return;
+    const uint4 h = reinterpret_cast<const uint4 *>(hist)[t];
+    const uint32_t local = h.x + h.y + h.z + h.w;
+    uint32_t S = local;  // keys in the bins of lanes <= t
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(S, off, 64);
+        if (t >= off) S += o;
+    }
+    const uint32_t p0 = S - local + h.x, p1 = p0 + h.y, p2 = p1 + h.z, p3 = p2 + h.w;
+    int d = -1;
+    uint32_t below = 0;
+    if (p0 >= need) { d = 4 * t; below = p0 - h.x; }
+    else if (p1 >= need) { d = 4 * t + 1; below = p1 - h.y; }
+    else if (p2 >= need) { d = 4 * t + 2; below = p2 - h.z; }
+    else if (p3 >= need) { d = 4 * t + 3; below = p3 - h.w; }
+    // prefix counts grow with the lane, so the lanes holding a digit are L .. 63
+    const unsigned long long m = __ballot(d >= 0);
+    if (t == __ffsll((long long)m) - 1) {
+        bc[0] = (uint32_t)d;
+        bc[1] = below;
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void hist_clear(uint32_t *hist, int t) {
+    for (int i = t; i < 256; i += NT) hist[i] = 0u;
+}
+
 // Select the K entries of largest |M| (ties: lower p) among the quantized rows
 // of the state held in x; write them sorted by p to the head's compensation
 // arrays and set them to 0 in x (so they are left out of both scale maxima
@@ -147,8 +218,11 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
     float thr = 0.0f;        // the K-th entry is (thr, pk)
     uint32_t pk = 0;
     bool exact = false;
+    int total = 0;  // candidates in LDS (when exact)
 
-    // 1) the K-th largest of the per-thread maxima bounds the K-th |M| from below
+    // 1) the K-th largest of the per-thread maxima bounds the K-th |M| from
+    //    below; two radix passes find its top 16 bits, t0 (its low bits
+    //    cleared: still a bound), and the largest maximum comes with them
     float tmax = -1.0f;
 #pragma unroll
     for (int r = 0; r < 8; ++r)
@@ -156,22 +230,32 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
         for (int c = 0; c < 8; ++c)
             if (rw.w[r] != 16) tmax = fmaxf(tmax, fabsf(x[r][c]));
     if (K <= NT) {
-        reinterpret_cast<float *>(sm.ckey)[t] = tmax;
+        // histogram bins in the entry-value array (unused until the chosen
+        // entries are gathered); the keys of magnitudes order like the values,
+        // and a thread without quantized entries has key 0
+        uint32_t *hist = reinterpret_cast<uint32_t *>(sm.cvl);
+        const uint32_t key = tmax >= 0.0f ? __float_as_uint(tmax) : 0u;
+        uint32_t lo = 0, need = K;
+        hist_clear<NT>(hist, t);
+        if (t == 0) sm.bc[3] = 0u;
         __syncthreads();
-        int rank = 0;  // thread maxima (value desc, thread asc) ahead of mine
-        for (int s2 = 0; s2 < NT; ++s2) {
-            const float o = reinterpret_cast<const float *>(sm.ckey)[s2];
-            rank += (o > tmax) || (o == tmax && s2 < t);
+        atomicMax(&sm.bc[3], key);
+        for (int shift = 24; shift >= 16; shift -= 8) {
+            if (((key ^ lo) & above_digit(shift)) == 0u) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            __syncthreads();
+            find_desc(hist, need, sm.bc, t);
+            __syncthreads();
+            lo |= sm.bc[0] << shift;
+            need -= sm.bc[1];
+            hist_clear<NT>(hist, t);
+            __syncthreads();
         }
-        if (rank == K - 1) sm.bc[0] = __float_as_uint(tmax);
-        if (rank == 0) sm.bc[2] = __float_as_uint(tmax);
-        __syncthreads();
-        const float t0 = __uint_as_float(sm.bc[0]);
-        const uint32_t kmax = sm.bc[2];
+        const float t0 = __uint_as_float(lo);
+        const uint32_t kmax = sm.bc[3];
         // 2) compact the candidates |M| >= t0 into LDS when they are few
-        const int mine = t0 >= 0.0f ? count_ge(x, rw, t0) : 0;
-        const int total = block_sum<NT>(mine, sm.red, phase);
-        if (t0 >= 0.0f && total <= kCandMax) {
+        const int mine = count_ge(x, rw, t0);
+        total = block_sum<NT>(mine, sm.red, phase);
+        if (total <= kCandMax) {
             if (t == 0) sm.bc[1] = 0;
             __syncthreads();
             int base = mine ? (int)atomicAdd(&sm.bc[1], (uint32_t)mine) : 0;
@@ -181,36 +265,60 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                 for (int c = 0; c < 8; ++c) {
                     const float v = fabsf(x[r][c]);
                     if (rw.w[r] != 16 && v >= t0) {
-                        reinterpret_cast<float *>(sm.ckey)[base] = v;
+                        sm.ckey[base] = __float_as_uint(v);
                         sm.cix[base] = pbase + (uint32_t)(c * DK + r);
+                        sm.csv[base] = x[r][c];
                         ++base;
                     }
                 }
             __syncthreads();
             // 3) the K-th candidate in the order (|M| descending, p ascending):
-            //    bit-serial search of its |M| pattern (every candidate lies in
-            //    [t0, largest], so the bits above the highest one where those
-            //    two differ are known), then of its p among the ties
-            constexpr int CB = kCandMax / NT >= 16 ? 5 : kCandMax / NT >= 8 ? 4 : 3;  // bits of a count
-            constexpr int PB = DK * DV > 8192 ? 14 : DK * DV > 4096 ? 13 : 12;           // bits of p
-            const uint32_t lo = __float_as_uint(t0);
+            //    radix passes over the |M| bits below the highest one where t0
+            //    and the largest candidate differ (the bits above are common to
+            //    every candidate), then, if some of its ties are left out,
+            //    over the p of those ties
             const int top = (lo ^ kmax) ? 31 - __builtin_clz(lo ^ kmax) : -1;
             uint32_t P = top >= 0 ? lo & ~((2u << top) - 1u) : lo;
-            for (int bit = top; bit >= 0; --bit) {
-                const uint32_t cand = P | (1u << bit);
-                int m = 0;
-                for (int e = t; e < total; e += NT) m += sm.ckey[e] >= cand;
-                if (block_count<NT, CB>(m, sm.red, phase) >= K) P = cand;
+            uint32_t ties = (uint32_t)total;  // candidates equal to P (all of them if top < 0)
+            need = K;
+            for (int shift = top >= 0 ? (top >> 3) << 3 : -8; shift >= 0; shift -= 8) {
+                const uint32_t hm = above_digit(shift);
+#pragma unroll
+                for (int k = 0; k < kCandMax / NT; ++k) {
+                    const int e = t + k * NT;
+                    if (e >= total) break;
+                    const uint32_t v = sm.ckey[e];
+                    if (((v ^ P) & hm) == 0u) atomicAdd(&hist[(v >> shift) & 255u], 1u);
+                }
+                __syncthreads();
+                find_desc(hist, need, sm.bc, t);
+                __syncthreads();
+                P |= sm.bc[0] << shift;
+                need -= sm.bc[1];
+                ties = sm.bc[2];
+                hist_clear<NT>(hist, t);
+                __syncthreads();
             }
-            int above = 0;
-            for (int e = t; e < total; e += NT) above += sm.ckey[e] > P;
-            const int need = K - block_count<NT, CB>(above, sm.red, phase);
-            uint32_t X = 0;
-            for (int bit = PB - 1; bit >= 0; --bit) {
-                const uint32_t cand = X | (1u << bit);
-                int m = 0;
-                for (int e = t; e < total; e += NT) m += (sm.ckey[e] == P) & (sm.cix[e] < cand);
-                if (block_count<NT, CB>(m, sm.red, phase) < need) X = cand;
+            uint32_t X = 0xffffffffu;  // every tie chosen
+            if (need < ties) {
+                X = 0;
+                for (int shift = 8; shift >= 0; shift -= 8) {
+                    const uint32_t hm = above_digit(shift);
+#pragma unroll
+                    for (int k = 0; k < kCandMax / NT; ++k) {
+                        const int e = t + k * NT;
+                        if (e >= total) break;
+                        const uint32_t q = sm.cix[e];
+                        if (sm.ckey[e] == P && ((q ^ X) & hm) == 0u) atomicAdd(&hist[(q >> shift) & 255u], 1u);
+                    }
+                    __syncthreads();
+                    find_asc(hist, need, sm.bc, t);
+                    __syncthreads();
+                    X |= sm.bc[0] << shift;
+                    need -= sm.bc[1];
+                    hist_clear<NT>(hist, t);
+                    __syncthreads();
+                }
             }
             thr = __uint_as_float(P);
             pk = X;
@@ -246,35 +354,81 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
         pk = X;
     }
 
-    // the chosen entries, then ranked by p for storage
+    // the chosen entries (index p in sp, value in sv), then ranked by p for
+    // storage; each is marked in a 64-bit mask per owner thread (bit 8 r + c
+    // of its block, kept in the column-partial array, unused until the
+    // requantization) and then set to 0 in x
+    uint32_t *sp = sm.cix;
+    float *sv = sm.cvl;
+    uint32_t *zm = reinterpret_cast<uint32_t *>(&sm.b.colp[0][0]);
     if (t == 0) sm.bc[1] = 0;
-    __syncthreads();
-    int mine = 0;
+    if (exact) {
+        // they are among the candidates in LDS: gathered from there (K <= NT
+        // here, so they fit in the histogram's array)
+        sp = reinterpret_cast<uint32_t *>(sm.cvl);
+        sv = sm.cvl + kKMax / 2;
+        zm[2 * t] = 0u;
+        zm[2 * t + 1] = 0u;
+        __syncthreads();
+        constexpr int CG = DV / 8;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-            mine += (rw.w[r] != 16) & chosen<DK>(fabsf(x[r][c]), pbase + (uint32_t)(c * DK + r), thr, pk);
-    int base = mine ? (int)atomicAdd(&sm.bc[1], (uint32_t)mine) : 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const uint32_t p = pbase + (uint32_t)(c * DK + r);
-            if (rw.w[r] != 16 && chosen<DK>(fabsf(x[r][c]), p, thr, pk)) {
-                sm.cix[base] = p;
-                sm.cvl[base] = x[r][c];
-                ++base;
-                x[r][c] = 0.0f;
+        for (int k = 0; k < kCandMax / NT; ++k) {
+            const int e = t + k * NT;
+            if (e >= total) break;
+            const uint32_t v = sm.ckey[e], p = sm.cix[e];
+            if (chosen<DK>(__uint_as_float(v), p, thr, pk)) {
+                const uint32_t slot = atomicAdd(&sm.bc[1], 1u);
+                sp[slot] = p;
+                sv[slot] = sm.csv[e];
+                const uint32_t j = p / DK, i = p - j * DK;
+                const uint32_t owner = (i >> 3) * CG + (j >> 3), bit = (i & 7u) * 8u + (j & 7u);
+                atomicOr(&zm[2 * owner + (bit >> 5)], 1u << (bit & 31u));
             }
         }
+    } else {
+        __syncthreads();
+        int mine = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                mine += (rw.w[r] != 16) & chosen<DK>(fabsf(x[r][c]), pbase + (uint32_t)(c * DK + r), thr, pk);
+        int base = mine ? (int)atomicAdd(&sm.bc[1], (uint32_t)mine) : 0;
+        uint32_t zlo = 0u, zhi = 0u;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t p = pbase + (uint32_t)(c * DK + r);
+                if (rw.w[r] != 16 && chosen<DK>(fabsf(x[r][c]), p, thr, pk)) {
+                    sm.cix[base] = p;
+                    sm.cvl[base] = x[r][c];
+                    ++base;
+                    const int bit = r * 8 + c;
+                    if (bit < 32) zlo |= 1u << bit; else zhi |= 1u << (bit - 32);
+                }
+            }
+        zm[2 * t] = zlo;
+        zm[2 * t + 1] = zhi;
+    }
+    __syncthreads();
+    {
+        const uint32_t zlo = zm[2 * t], zhi = zm[2 * t + 1];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int bit = r * 8 + c;
+                if (((bit < 32 ? zlo >> bit : zhi >> (bit - 32)) & 1u) != 0u) x[r][c] = 0.0f;
+            }
+    }
     __syncthreads();
     for (int e = t; e < K; e += NT) {
-        const uint32_t p = sm.cix[e];
+        const uint32_t p = sp[e];
         int rank = 0;
-        for (int f = 0; f < K; ++f) rank += sm.cix[f] < p;
+        for (int f = 0; f < K; ++f) rank += sp[f] < p;
         reinterpret_cast<uint16_t *>(R + hd.cidx)[rank] = (uint16_t)p;
-        reinterpret_cast<float *>(R + hd.cval)[rank] = sm.cvl[e];
+        reinterpret_cast<float *>(R + hd.cval)[rank] = sv[e];
     }
     __syncthreads();
 }

@@ -66,12 +66,24 @@ def _counter(d: str, name: str):
         grid[did] = int(r["Grid_Size"])
     step = [per[i] for i in sorted(per) if _is_step(kern[i])]
     step_names = sorted({kern[i] for i in per if _is_step(kern[i])})
+    by_kernel = defaultdict(float)
+    for i in per:
+        if _is_step(kern[i]):
+            by_kernel[_short(kern[i])] += per[i]
     # The runtime also issues small copies of its own (argument uploads); the
     # calibration copies are the ones with the largest grid.
     copies = [i for i in per if COPY_KERNEL in kern[i]]
     big = max((grid[i] for i in copies), default=0)
     copy = [per[i] for i in sorted(copies) if grid[i] == big]
-    return step, step_names, copy
+    return step, step_names, copy, by_kernel
+
+
+def _short(name: str) -> str:
+    """k_win, k_win_end, k_step, k_step_lag from a demangled kernel name."""
+    for k in ("::k_win_end<", "::k_win<", "::k_step_lag<", "::k_step<"):
+        if k in name:
+            return k[2:-1]
+    return name
 
 
 def _source_hash() -> str:
@@ -85,8 +97,8 @@ def counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, cmd
     import bench
     import synth
     w = synth.WORKLOADS[workload]
-    f_step, names, f_copy = _counter(fetch_dir, "FETCH_SIZE")
-    w_step, _, w_copy = _counter(write_dir, "WRITE_SIZE")
+    f_step, names, f_copy, f_by = _counter(fetch_dir, "FETCH_SIZE")
+    w_step, _, w_copy, w_by = _counter(write_dir, "WRITE_SIZE")
     if not f_copy or not w_copy:
         raise SystemExit("the calibration copy kernel is missing from the counter runs")
     kernels_per_call = 2 if w.window > 1 else 1
@@ -112,6 +124,13 @@ def counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, cmd
              f"hbm_bytes_per_launch: {rd + wr:.0f}",
              f"algorithmic_bytes_per_launch: {alg:.0f}",
              f"traffic_over_algorithmic: {(rd + wr) / alg:.4f}"]
+    if len(f_by) > 1:
+        # one stq_decode_step call launches several kernels: bytes of each
+        for k in sorted(f_by):
+            kr = f_by[k] / calls_f * 1024 * fetch_scale
+            kw = w_by.get(k, 0.0) / calls_w * 1024 * write_scale
+            lines.append(f"{k}_read_bytes_per_call: {kr:.0f}")
+            lines.append(f"{k}_write_bytes_per_call: {kw:.0f}")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -120,8 +139,8 @@ def valu(d: str, workload: str, cmd: str, out: str) -> None:
     sys.path.insert(0, ROOT)
     import synth
     w = synth.WORKLOADS[workload]
-    insts, names, _ = _counter(d, "SQ_INSTS_VALU")
-    waves, _, _ = _counter(d, "SQ_WAVES")
+    insts, names, _, _ = _counter(d, "SQ_INSTS_VALU")
+    waves, _, _, _ = _counter(d, "SQ_WAVES")
     if not insts or not waves:
         raise SystemExit("no decode-kernel dispatch in the counter run")
     # one stq_decode_step call launches k_win and k_win_end in the windowed mode

@@ -149,6 +149,12 @@ WORKLOADS = {
         row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.02,
         init="zero", layers=4, scale_fit="lagged",
         desc="the serving pool with lagged scales (written with the previous state's fit)"),
+    "kimi_serving": Workload(
+        "kimi_serving", 12, B=512, H=32, dk=128, dv=128, T=256, unit="keyrow", gate="keyvec",
+        row_scale="f16", col_scale="f16", io="bf16", bits="avg4", pivot_frac=0.01,
+        init="outlier", layers=4,
+        desc="the KDA layer at serving scale: B=512, four layers (1.3 GB of state, beyond the "
+             "256 MB last-level cache), per-key-row avg 4 bit, 1% pivot rows"),
     "kda_lifetimes": Workload(
         "kda_lifetimes", 10, B=256, H=32, dk=128, dv=128, T=256, unit="keyrow", gate="keyvec",
         row_scale="f16", col_scale="f16", io="bf16", bits="allocated", pivot_frac=0.01,

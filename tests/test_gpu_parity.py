@@ -215,20 +215,20 @@ def _both_kinds_bits(d):
 
 
 def _expected_groups(bits):
-    """Heads whose rows are all 4-bit in pairs, in head order; every other
-    head alone; an unpaired 4-bit head last."""
-    groups, pending = [], None
+    """Heads whose rows are all 4-bit in pairs, in head order, first; then
+    every other head alone, in head order; an unpaired 4-bit head last."""
+    pairs, singles, pending = [], [], None
     for h, r in enumerate(bits):
         if not (r == 4).all():
-            groups.append((h, 0xFFFF))
+            singles.append((h, 0xFFFF))
         elif pending is None:
             pending = h
         else:
-            groups.append((pending, h))
+            pairs.append((pending, h))
             pending = None
     if pending is not None:
-        groups.append((pending, 0xFFFF))
-    return groups
+        singles.append((pending, 0xFFFF))
+    return pairs + singles
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -295,6 +295,15 @@ def test_kimi_kda_sampled_units_all_256_steps():
     """Full KDA batch, 256 followed units over all 256 steps."""
     w = synth.WORKLOADS["kimi_kda"]
     _run_sampled(w, w.T, 256, seed=12, tag="kimi-long")
+
+
+def test_kimi_serving_sampled_units():
+    """The KDA layer at serving scale (B=512, 4-bit rows with FP16 pivot
+    rows, layers 0 and 3 of four, whose pivot maps differ): 128 followed units
+    over 64 steps each, slot bytes compared at the end."""
+    w = synth.WORKLOADS["kimi_serving"]
+    for layer in (0, 3):
+        _run_sampled(w, 64, 128, seed=71 + layer, layer=layer, tag=f"kimi-serving-{layer}")
 
 
 def test_unpack_and_pack_match_oracle():
@@ -563,6 +572,42 @@ def test_windowed_zero_state_ties():
         for t in range(5):
             o_gpu, o_ref = hs.step(hs.load_full(t))
             _check_step(o_gpu, o_ref, hs.follow, t, "win-zero")
+            assert not hs.compare_slots(), t
+    finally:
+        hs.close()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_windowed_tied_outliers(d):
+    """Selections whose K-th magnitude is tied among candidates: per state,
+    N(0, 0.1^2) entries plus 30 entries of magnitude 5 and 200 of magnitude
+    3 (random signs and places), so the 82 entries (40 at d = 64) take the
+    30 largest and, of the 200 ties, those of lowest index.  Pack, then
+    steps across two window ends (W = 4); slot bytes and outputs equal the
+    oracle's after every step."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    K = 82 if d == 128 else 40
+    w = synth.WORKLOADS["windowed_kda"].with_(B=3, H=4, dk=d, dv=d, window=4, comps=K,
+                                              name=f"win_ties_d{d}")
+    print(f"[win-ties] d={d} K={K}", flush=True)
+    hs = _harness(w)
+    try:
+        rng = np.random.default_rng(11 + d)
+        M = (rng.standard_normal((w.B, w.H, d, d)) * 0.1).astype(np.float32)
+        for b in range(w.B):
+            for h in range(w.H):
+                pos = rng.choice(d * d, 230, replace=False)
+                mag = np.where(np.arange(230) < 30, 5.0, 3.0).astype(np.float32)
+                sign = np.where(rng.random(230) < 0.5, -1.0, 1.0).astype(np.float32)
+                M[b, h].reshape(-1)[pos] = mag * sign
+        stq.pack(hs.pool, hs.slot_ids, torch.from_numpy(M).cuda())
+        for b, h in hs.follow:
+            hs.ocfg.pack_head(hs.oslots[b], h, M[b, h])
+        assert not hs.compare_slots()
+        for t in range(9):
+            o_gpu, o_ref = hs.step(hs.load_full(t))
+            _check_step(o_gpu, o_ref, hs.follow, t, "win-ties")
             assert not hs.compare_slots(), t
     finally:
         hs.close()
