@@ -117,6 +117,15 @@ __device__ __forceinline__ int lower_bound(const uint32_t *a, int n, uint32_t x)
 // fallback search uses.  Linear index p = j*d_k + i; the thread's entry (r, c)
 // has p = pbase + c*d_k + r with pbase = 8*cg*d_k + 8*rg.
 
+// Hides the block's values from the optimizer: magnitudes computed before are
+// not carried to later uses (64 more live registers), they are formed again.
+__device__ __forceinline__ void opaque_block(float (&x)[8][8]) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(x[r][c]));
+}
+
 // Number of the thread's quantized entries with |M| >= thr.
 __device__ __forceinline__ int count_ge(const float (&x)[8][8], const Rows &rw, float thr) {
     int n = 0;
@@ -135,67 +144,55 @@ __device__ __forceinline__ bool chosen(float v, uint32_t p, float thr, uint32_t 
 }
 
 // Radix selection with LDS histograms of 256 bins (8-bit digits).  A pass
-// histograms one digit of the keys that match the digits found so far; one
-// wave then scans the bins (lane l owns bins 4l .. 4l+3) and broadcasts the
-// digit through bc.
+// histograms one digit of the keys that match the digits found so far; after
+// one barrier every wave scans the bins itself (lane l owns bins 4l .. 4l+3),
+// so the digit needs no broadcast.  Three histograms rotate: pass k fills
+// hist k % 3 and clears hist (k + 1) % 3, last read in pass k - 2, whose scans
+// every wave finished before the barrier of pass k - 1.
 
 // Bits above digit `shift` (the digits already found).
 __device__ __forceinline__ uint32_t above_digit(int shift) { return shift >= 24 ? 0u : ~0u << (shift + 8); }
 
-// Largest digit d with (count of bins >= d) >= need: bc[0] = d, bc[1] = the
-// count in bins above d, bc[2] = the count in bin d.  need >= 1 and the
-// histogram holds at least need keys.
-__device__ __forceinline__ void find_desc(const uint32_t *hist, uint32_t need, uint32_t *bc, int t) {
-    if (t >= 64) return;
-    const uint4 h = reinterpret_cast<const uint4 *>(hist)[t];
-    const uint32_t local = h.x + h.y + h.z + h.w;
-    uint32_t S = local;  // keys in the bins of lanes >= t
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(S, off, 64);
-        if (t + off < 64) S += o;
-    }
-    const uint32_t s3 = S - local + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
-    int d = -1;
-    uint32_t above = 0, eq = 0;
-    if (s3 >= need) { d = 4 * t + 3; above = s3 - h.w; eq = h.w; }
-    else if (s2 >= need) { d = 4 * t + 2; above = s2 - h.z; eq = h.z; }
-    else if (s1 >= need) { d = 4 * t + 1; above = s1 - h.y; eq = h.y; }
-    else if (s0 >= need) { d = 4 * t; above = s0 - h.x; eq = h.x; }
-    // suffix counts fall with the lane, so the lanes holding a digit are 0 .. L
-    const unsigned long long m = __ballot(d >= 0);
-    if (t == 63 - __clzll(m)) {
-        bc[0] = (uint32_t)d;
-        bc[1] = above;
-        bc[2] = eq;
-    }
-}
+struct Digit {
+    uint32_t d;      // the digit
+    uint32_t other;  // descending: keys in bins above d; ascending: keys in bins below d
+    uint32_t eq;     // keys in bin d
+};
 
-// Smallest digit d with (count of bins <= d) >= need: bc[0] = d, bc[1] = the
-// count in bins below d.
-__device__ __forceinline__ void find_asc(const uint32_t *hist, uint32_t need, uint32_t *bc, int t) {
-    if (t >= 64) return;
-    const uint4 h = reinterpret_cast<const uint4 *>(hist)[t];
+// Largest digit d with (keys in bins >= d) >= need (DESC), or smallest digit
+// d with (keys in bins <= d) >= need (ascending).  need >= 1 and the
+// histogram holds at least need keys.  Called by every lane of a wave.
+template <bool DESC>
+__device__ __forceinline__ Digit find_digit(const uint32_t *hist, uint32_t need, int lane) {
+    const uint4 h = reinterpret_cast<const uint4 *>(hist)[lane];
     const uint32_t local = h.x + h.y + h.z + h.w;
-    uint32_t S = local;  // keys in the bins of lanes <= t
+    uint32_t S = local;  // keys in the bins of lanes >= lane (DESC) or <= lane
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(S, off, 64);
-        if (t >= off) S += o;
+        const uint32_t o = DESC ? __shfl_down(S, off, 64) : __shfl_up(S, off, 64);
+        if (DESC ? lane + off < 64 : lane >= off) S += o;
     }
-    const uint32_t p0 = S - local + h.x, p1 = p0 + h.y, p2 = p1 + h.z, p3 = p2 + h.w;
     int d = -1;
-    uint32_t below = 0;
-    if (p0 >= need) { d = 4 * t; below = p0 - h.x; }
-    else if (p1 >= need) { d = 4 * t + 1; below = p1 - h.y; }
-    else if (p2 >= need) { d = 4 * t + 2; below = p2 - h.z; }
-    else if (p3 >= need) { d = 4 * t + 3; below = p3 - h.w; }
-    // prefix counts grow with the lane, so the lanes holding a digit are L .. 63
-    const unsigned long long m = __ballot(d >= 0);
-    if (t == __ffsll((long long)m) - 1) {
-        bc[0] = (uint32_t)d;
-        bc[1] = below;
+    uint32_t other = 0, eq = 0;
+    if (DESC) {
+        const uint32_t s3 = S - local + h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
+        if (s3 >= need) { d = 4 * lane + 3; other = s3 - h.w; eq = h.w; }
+        else if (s2 >= need) { d = 4 * lane + 2; other = s2 - h.z; eq = h.z; }
+        else if (s1 >= need) { d = 4 * lane + 1; other = s1 - h.y; eq = h.y; }
+        else if (s0 >= need) { d = 4 * lane; other = s0 - h.x; eq = h.x; }
+    } else {
+        const uint32_t p0 = S - local + h.x, p1 = p0 + h.y, p2 = p1 + h.z, p3 = p2 + h.w;
+        if (p0 >= need) { d = 4 * lane; other = p0 - h.x; eq = h.x; }
+        else if (p1 >= need) { d = 4 * lane + 1; other = p1 - h.y; eq = h.y; }
+        else if (p2 >= need) { d = 4 * lane + 2; other = p2 - h.z; eq = h.z; }
+        else if (p3 >= need) { d = 4 * lane + 3; other = p3 - h.w; eq = h.w; }
     }
+    // the counts are monotone over the lanes, so the lanes holding a digit
+    // are 0 .. L (DESC: the answer is lane L) or L .. 63 (the answer is L)
+    const unsigned long long m = __ballot(d >= 0);
+    const int L = DESC ? 63 - __clzll((long long)m) : __ffsll((long long)m) - 1;
+    return Digit{(uint32_t)__shfl(d, L, 64), (uint32_t)__shfl((int)other, L, 64),
+                 (uint32_t)__shfl((int)eq, L, 64)};
 }
 
 template <int NT>
@@ -230,30 +227,32 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
         for (int c = 0; c < 8; ++c)
             if (rw.w[r] != 16) tmax = fmaxf(tmax, fabsf(x[r][c]));
     if (K <= NT) {
-        // histogram bins in the entry-value array (unused until the chosen
+        // three histograms in the entry-value array (unused until the chosen
         // entries are gathered); the keys of magnitudes order like the values,
         // and a thread without quantized entries has key 0
-        uint32_t *hist = reinterpret_cast<uint32_t *>(sm.cvl);
+        uint32_t *hists = reinterpret_cast<uint32_t *>(sm.cvl);
+        int pass = 0;
+        const int lane = t & 63;
         const uint32_t key = tmax >= 0.0f ? __float_as_uint(tmax) : 0u;
         uint32_t lo = 0, need = K;
-        hist_clear<NT>(hist, t);
+        hist_clear<NT>(hists, t);
         if (t == 0) sm.bc[3] = 0u;
         __syncthreads();
         atomicMax(&sm.bc[3], key);
-        for (int shift = 24; shift >= 16; shift -= 8) {
+        for (int shift = 24; shift >= 16; shift -= 8, ++pass) {
+            uint32_t *hist = hists + 256 * (pass % 3);
+            hist_clear<NT>(hists + 256 * ((pass + 1) % 3), t);
             if (((key ^ lo) & above_digit(shift)) == 0u) atomicAdd(&hist[(key >> shift) & 255u], 1u);
             __syncthreads();
-            find_desc(hist, need, sm.bc, t);
-            __syncthreads();
-            lo |= sm.bc[0] << shift;
-            need -= sm.bc[1];
-            hist_clear<NT>(hist, t);
-            __syncthreads();
+            const Digit g = find_digit<true>(hist, need, lane);
+            lo |= g.d << shift;
+            need -= g.other;
         }
         const float t0 = __uint_as_float(lo);
         const uint32_t kmax = sm.bc[3];
         // 2) compact the candidates |M| >= t0 into LDS when they are few
         const int mine = count_ge(x, rw, t0);
+        opaque_block(x);
         total = block_sum<NT>(mine, sm.red, phase);
         if (total <= kCandMax) {
             if (t == 0) sm.bc[1] = 0;
@@ -271,6 +270,7 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                         ++base;
                     }
                 }
+            opaque_block(x);
             __syncthreads();
             // 3) the K-th candidate in the order (|M| descending, p ascending):
             //    radix passes over the |M| bits below the highest one where t0
@@ -281,7 +281,9 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
             uint32_t P = top >= 0 ? lo & ~((2u << top) - 1u) : lo;
             uint32_t ties = (uint32_t)total;  // candidates equal to P (all of them if top < 0)
             need = K;
-            for (int shift = top >= 0 ? (top >> 3) << 3 : -8; shift >= 0; shift -= 8) {
+            for (int shift = top >= 0 ? (top >> 3) << 3 : -8; shift >= 0; shift -= 8, ++pass) {
+                uint32_t *hist = hists + 256 * (pass % 3);
+                hist_clear<NT>(hists + 256 * ((pass + 1) % 3), t);
                 const uint32_t hm = above_digit(shift);
 #pragma unroll
                 for (int k = 0; k < kCandMax / NT; ++k) {
@@ -291,18 +293,17 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                     if (((v ^ P) & hm) == 0u) atomicAdd(&hist[(v >> shift) & 255u], 1u);
                 }
                 __syncthreads();
-                find_desc(hist, need, sm.bc, t);
-                __syncthreads();
-                P |= sm.bc[0] << shift;
-                need -= sm.bc[1];
-                ties = sm.bc[2];
-                hist_clear<NT>(hist, t);
-                __syncthreads();
+                const Digit g = find_digit<true>(hist, need, lane);
+                P |= g.d << shift;
+                need -= g.other;
+                ties = g.eq;
             }
             uint32_t X = 0xffffffffu;  // every tie chosen
             if (need < ties) {
                 X = 0;
-                for (int shift = 8; shift >= 0; shift -= 8) {
+                for (int shift = 8; shift >= 0; shift -= 8, ++pass) {
+                    uint32_t *hist = hists + 256 * (pass % 3);
+                    hist_clear<NT>(hists + 256 * ((pass + 1) % 3), t);
                     const uint32_t hm = above_digit(shift);
 #pragma unroll
                     for (int k = 0; k < kCandMax / NT; ++k) {
@@ -312,14 +313,13 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
                         if (sm.ckey[e] == P && ((q ^ X) & hm) == 0u) atomicAdd(&hist[(q >> shift) & 255u], 1u);
                     }
                     __syncthreads();
-                    find_asc(hist, need, sm.bc, t);
-                    __syncthreads();
-                    X |= sm.bc[0] << shift;
-                    need -= sm.bc[1];
-                    hist_clear<NT>(hist, t);
-                    __syncthreads();
+                    const Digit g = find_digit<false>(hist, need, lane);
+                    X |= g.d << shift;
+                    need -= g.other;
                 }
             }
+            // the histograms are read until here: the gather below reuses them
+            __syncthreads();
             thr = __uint_as_float(P);
             pk = X;
             exact = true;
@@ -328,8 +328,11 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
     if (!exact) {
         // fallback: bit-serial search of the K-th |M| over the whole state,
         // then of the tie position
+        // (opaque_block in the loops: per-entry values hoisted out of them
+        // would hold a register each for the whole loop)
         uint32_t P = 0;
         for (int bit = 30; bit >= 0; --bit) {
+            opaque_block(x);
             const uint32_t cand = P | (1u << bit);
             if (block_sum<NT>(count_ge(x, rw, __uint_as_float(cand)), sm.red, phase) >= K) P = cand;
         }
@@ -342,6 +345,7 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
         const int need = K - block_sum<NT>(above, sm.red, phase);
         uint32_t X = 0;
         for (int bit = 15; bit >= 0; --bit) {
+            opaque_block(x);
             const uint32_t cand = X | (1u << bit);
             int m2 = 0;
 #pragma unroll
@@ -425,8 +429,15 @@ __device__ void select_comps(const Args &A, const HeadDesc &hd, uint8_t *R, cons
     __syncthreads();
     for (int e = t; e < K; e += NT) {
         const uint32_t p = sp[e];
+        // rank = entries of smaller index, four per LDS read (sp is 16-byte aligned)
         int rank = 0;
-        for (int f = 0; f < K; ++f) rank += sp[f] < p;
+        const uint4 *s4 = reinterpret_cast<const uint4 *>(sp);
+#pragma unroll 4
+        for (int f = 0; f < (K >> 2); ++f) {
+            const uint4 q = s4[f];
+            rank += (int)(q.x < p) + (int)(q.y < p) + (int)(q.z < p) + (int)(q.w < p);
+        }
+        for (int f = K & ~3; f < K; ++f) rank += sp[f] < p;
         reinterpret_cast<uint16_t *>(R + hd.cidx)[rank] = (uint16_t)p;
         reinterpret_cast<float *>(R + hd.cval)[rank] = sv[e];
     }
