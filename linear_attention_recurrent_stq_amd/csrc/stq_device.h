@@ -450,12 +450,13 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
     if (IMP && cs) {
         float om[8];
         lds_read8(&sm.om[8 * rg], om, 0);
+        const bool all_q = !per_row<W>() || fw;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             float m = 0.0f;
 #pragma unroll
             for (int r = 0; r < 8; ++r)
-                if (row_w<W>(rw, r) != 16) m = fmaxf(m, om[r] * fabsf(x[r][c]));
+                if (all_q || row_w<W>(rw, r) != 16) m = fmaxf(m, om[r] * fabsf(x[r][c]));
             sm.colm[c][t] = m;
         }
     } else if (cs && (!per_row<W>() || fw)) {
@@ -468,14 +469,31 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
             sm.colm[c][t] = m;
         }
     } else if (cs) {
+        // rows of differing widths: a pair of rows that holds no pivot row in
+        // any block of the wave (a wave-uniform test) takes the unmasked
+        // max3, the others a per-lane test
+        uint32_t wm = 0u;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float m = 0.0f;
+        for (int r = 0; r < 8; ++r) wm |= (__any(row_w<W>(rw, r) == 16) ? 1u : 0u) << r;
+        float m[8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                if (row_w<W>(rw, r) != 16) m = fmaxf(m, fabsf(x[r][c]));
-            sm.colm[c][t] = m;
+        for (int c = 0; c < 8; ++c) m[c] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+            if (((wm >> r) & 3u) == 0u) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) m[c] = fmaxf(m[c], fmaxf(fabsf(x[r][c]), fabsf(x[r + 1][c])));
+            } else {
+                const bool q0 = row_w<W>(rw, r) != 16, q1 = row_w<W>(rw, r + 1) != 16;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    if (q0) m[c] = fmaxf(m[c], fabsf(x[r][c]));
+                    if (q1) m[c] = fmaxf(m[c], fabsf(x[r + 1][c]));
+                }
+            }
         }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sm.colm[c][t] = m[c];
     }
     if (cs || emit_o) __syncthreads();
     // o of column t, and the new scale of column tc: with at least 2 d_v
