@@ -90,17 +90,21 @@ def launch_bytes(w: synth.Workload, bits: np.ndarray) -> float:
 
 INIT_REQUESTS = 32  # requests whose outlier initial states are drawn (then repeated)
 
-# the sources the device code is compiled from (host-only files excluded)
-DEVICE_SOURCES = ("stq_device.h", "stq_internal.h", "stq_kernels.hip", "stq_window.hip")
+# the sources each decode kernel is compiled from (host-only files excluded):
+# the every-step kernels and the windowed ones share only the device headers
+STEP_SOURCES = ("stq_device.h", "stq_internal.h", "stq_kernels.hip")
+WINDOW_SOURCES = ("stq_device.h", "stq_internal.h", "stq_window.hip")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(w: synth.Workload | None = None) -> str:
+    """Hash of the device sources of the workload's decode kernels (every
+    device source without a workload)."""
     import hashlib
+    files = (WINDOW_SOURCES if w.window > 1 else STEP_SOURCES) if w is not None \
+        else tuple(sorted(set(STEP_SOURCES + WINDOW_SOURCES)))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrent_stq_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f not in DEVICE_SOURCES and not f.endswith(".hip"):
-            continue
+    for f in sorted(files):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -122,7 +126,7 @@ def counter_traffic(w: synth.Workload):
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash(w):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

@@ -44,7 +44,7 @@ def stats(d: str, workload: str, cmd: str, out: str) -> None:
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
     lines = [f"# rocprofv3 kernel-trace statistics, workload {workload}",
              f"# command: {cmd}",
-             f"# kernel_source_sha256: {_source_hash()}",
+             f"# kernel_source_sha256: {_source_hash(workload)}",
              "kernel | calls | average_us | min_us | max_us | percent"]
     for r in rows:
         lines.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -86,10 +86,12 @@ def _short(name: str) -> str:
     return name
 
 
-def _source_hash() -> str:
+def _source_hash(workload: str) -> str:
+    """Hash of the device sources of the workload's decode kernels."""
     sys.path.insert(0, ROOT)
     import bench
-    return bench.kernel_source_hash()
+    import synth
+    return bench.kernel_source_hash(synth.WORKLOADS[workload])
 
 
 def counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, cmd: str, out: str) -> None:
@@ -115,7 +117,7 @@ def counters(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, cmd
              f"device copy of {copy_bytes} bytes in the same run",
              f"workload: {workload}",
              f"kernels: {', '.join(names)}",
-             f"kernel_source_sha256: {_source_hash()}",
+             f"kernel_source_sha256: {_source_hash(workload)}",
              f"calls_measured: {calls_f}",
              f"fetch_scale: {fetch_scale:.4f}",
              f"write_scale: {write_scale:.4f}",
@@ -152,7 +154,7 @@ def valu(d: str, workload: str, cmd: str, out: str) -> None:
              f"# command: {cmd}",
              f"workload: {workload}",
              f"kernels: {', '.join(names)}",
-             f"kernel_source_sha256: {_source_hash()}",
+             f"kernel_source_sha256: {_source_hash(workload)}",
              f"calls_measured: {calls}",
              f"sq_insts_valu_per_launch: {per_launch:.0f}",
              f"sq_waves_per_launch: {waves_per_launch:.0f}",
