@@ -144,7 +144,13 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r));
+        for (int r = 0; r < 8; ++r) {
+            // per-row widths: FP16 pivot rows (16 bytes a piece, rare) are
+            // loaded when they are dequantized, so the block holds at most 8
+            // bytes a row
+            if (W == 0 && row_w<W>(rw, r) == 16) raw[r] = make_uint4(0, 0, 0, 0);
+            else raw[r] = load_piece(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r));
+        }
     }
 
     // per key row and per value column constants, computed once per state
@@ -213,7 +219,8 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             } else if (w == 16) {
                 const float a = sm.af[i];
                 // kW4P: a second pivot row of the block is loaded here (rare)
-                const uint4 pc = W != kW4P ? raw[r] : r == pr ? pv : load_piece(R + row_o<DV, W>(rw, r), cg, 16);
+                const uint4 pc = W == kW4P ? (r == pr ? pv : load_piece(R + row_o<DV, W>(rw, r), cg, 16))
+                               : W == 0 ? load_piece(R + row_o<DV, W>(rw, r), cg, 16) : raw[r];
                 const uint32_t hv[4] = {pc.x, pc.y, pc.z, pc.w};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -336,8 +343,11 @@ __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
     }
 }
 
+// The per-row class (MIX 2) is held to four waves per SIMD, the other
+// classes' occupancy: a couple of spilled registers cost less than a wave.
 template <int DK, int DV, int MIX, bool IMP = false>
-__global__ void __launch_bounds__(DK * DV / 64) k_step(Args A) {
+__global__ void __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_eu(MIX == 2 ? 4 : 1)))
+k_step(Args A) {
     __shared__ Lds<DK, DV> sm;
     step_groups<DK, DV, MIX, false, IMP>(A, sm);
 }
