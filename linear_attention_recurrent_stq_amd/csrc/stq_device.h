@@ -44,6 +44,36 @@ constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic rounds x to an 
 
 __device__ __forceinline__ float fma_(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 
+// Correctly rounded reciprocal and quotient of values with at most 11
+// significant bits (fp16 values, small integers): a reciprocal estimate
+// (v_rcp_f32, within an ulp) refined by one Newton step, then one correction
+// of the quotient.  The exact quotient of two such values is never within
+// 2^-36 (relative) of a midpoint between neighbouring floats, unless it is a
+// float itself, and the refined value is within about 2^-46 of it, so its
+// rounding is the correctly rounded quotient -- what an IEEE division gives.
+// The residuals 1 - b r and a - b q are exact (fma of operands this short).
+__device__ __forceinline__ float recip_h(float b) {
+    const float r = __builtin_amdgcn_rcpf(b);
+    const float e = fma_(-b, r, 1.0f);
+    return fma_(e, r, r);
+}
+__device__ __forceinline__ float div_h(float a, float b) {
+    const float y = recip_h(b);
+    const float q = a * y;
+    return fma_(fma_(-b, q, a), y, q);
+}
+// RN(a / n) for n = 2^(w-1) - 1 (7, 31 or 127) and any fp32 a: with y = RN(1/n)
+// one correction gives the correctly rounded quotient (a/n is a float, or it
+// is at least 2^-32 (relative) from a midpoint, n being odd and below 2^7);
+// an infinite a passes through as a division would give it.
+__device__ __forceinline__ float div_qmax(float a, int w) {
+    const float n = (float)((1 << (w - 1)) - 1);
+    const float y = w == 4 ? 1.0f / 7.0f : w == 6 ? 1.0f / 31.0f : 1.0f / 127.0f;
+    const float q = a * y;
+    const float c = fma_(fma_(-n, q, a), y, q);
+    return __builtin_isinf(q) ? q : c;
+}
+
 // H(x): fp16 nearest-even after saturating to +-65504; returns the pattern.
 __device__ __forceinline__ uint32_t h16(float x) {
     x = fminf(fmaxf(x, -65504.0f), 65504.0f);
@@ -515,7 +545,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
             if (A.lagged) reinterpret_cast<float *>(R + hd.scs)[tc] = Cs;
             const uint32_t hc = h16(Cs);
             const float cv = f16v(hc);
-            ic = cv > 0.0f ? sj / cv : 0.0f;
+            ic = cv > 0.0f ? div_h(sj, cv) : 0.0f;  // sj and cv are fp16 values
             reinterpret_cast<uint16_t *>(R + hd.cs)[tc] = (uint16_t)hc;
         }
         sm.ic[tc] = ic;
@@ -558,15 +588,16 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
         if (w != 16) {
             const float Rm = row_max<DK, DV>(sm, t);
             if (A.lagged) reinterpret_cast<float *>(R + hd.srs)[t] = Rm;
-            const float rq = Rm / (float)((1 << (w - 1)) - 1);
+            const float rq = div_qmax(Rm, w);
             if (A.rs16) {
                 rv = f16v(h16up(rq));
                 sat = rq > 65504.0f;
+                ir = rv > 0.0f ? recip_h(rv) : 0.0f;  // rv is an fp16 value
             } else {
                 rv = rq;
+                ir = rv > 0.0f ? 1.0f / rv : 0.0f;
+                if (__builtin_isinf(ir)) ir = 0.0f;
             }
-            ir = rv > 0.0f ? 1.0f / rv : 0.0f;
-            if (__builtin_isinf(ir)) ir = 0.0f;
         }
         if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)h16(rv);
         else reinterpret_cast<float *>(R + hd.rs)[t] = rv;

@@ -177,7 +177,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         const float c = dec_scale(in.c, 1, t & 1);
         const float sc = (quant && A.cs16 && c > 0.0f) ? c : 1.0f;
         sm.cf[t] = sc;
-        sm.isf[t] = 1.0f / sc;
+        sm.isf[t] = recip_h(sc);  // sc is an fp16 value or 1
         vv = dec_io(in.v, A.io_bf16, t & 1);
     }
     keep_inputs(in);
