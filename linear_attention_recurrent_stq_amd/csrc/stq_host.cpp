@@ -10,6 +10,7 @@
 // [K] fp32, delta values [W][d_v] and delta keys [W][d_k] (fp32); for lagged
 // scales (when the head has a quantized row) the next row scales, next column
 // scales, row statistics [d_k] fp32 and column statistics [d_v] fp32.
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -17,6 +18,7 @@
 #include <vector>
 
 #include "stq.h"
+
 #include "stq_internal.h"
 
 struct stq_layout {
@@ -28,13 +30,18 @@ struct stq_layout {
     std::vector<uint32_t> rows;         // [H*d_k] row table
     std::vector<uint32_t> groups;       // step-kernel head groups (h1 | h2 << 16)
     std::vector<float> omega;           // row-impact weights [H*d_k] (empty: none)
-    std::vector<uint8_t> table;         // device image: heads, rows, groups, weights; 256-B padded
+    std::vector<uint8_t> table;         // device image: heads, rows, groups, weights, (windowed)
+                                        // window-end flag; 256-B padded
+    size_t flag_off = 0;                // windowed: byte offset of the window-end flag (8 bytes)
     size_t slot_bytes = 0;
 };
 
 namespace {
 
 thread_local std::string g_err;
+// Windowed decode calls of the process, numbered from 1: the token a call's
+// in-window step leaves in the pool's window-end flag.
+std::atomic<uint64_t> g_token{0};
 
 stq_status fail(stq_status s, const std::string &msg) {
     g_err = msg;
@@ -132,6 +139,7 @@ stq::Args base_args(const stq_pool *p, int32_t B, const int32_t *ids) {
     a.window = L->cfg.window;
     a.comps = L->cfg.comps;
     a.lagged = L->cfg.scale_fit == STQ_FIT_LAGGED;
+    if (L->cfg.window > 1) a.end_flag = reinterpret_cast<uint64_t *>(base + L->flag_off);
     return a;
 }
 
@@ -331,7 +339,11 @@ stq_status stq_pack_layout(const stq_config *cfg, stq_layout **out) {
     const size_t hb = sizeof(stq::HeadDesc) * H, rb = sizeof(uint32_t) * (size_t)H * dk;
     const size_t gb = sizeof(uint32_t) * L->groups.size();
     const size_t ob = sizeof(float) * L->omega.size();
-    L->table.assign(up(hb + rb + gb + ob, 256), 0);
+    // windowed layouts: an 8-byte window-end flag after the tables, 0 until a
+    // call sets it (call tokens start at 1)
+    L->flag_off = up(hb + rb + gb + ob, 8);
+    const size_t fb = cfg->window > 1 ? 8 : 0;
+    L->table.assign(up(L->flag_off + fb, 256), 0);
     std::memcpy(L->table.data(), L->heads.data(), hb);
     std::memcpy(L->table.data() + hb, L->rows.data(), rb);
     std::memcpy(L->table.data() + hb + rb, L->groups.data(), gb);
@@ -409,8 +421,10 @@ stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slo
     a.beta = d_beta;
     a.o = d_o;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (L->cfg.window > 1)
+    if (L->cfg.window > 1) {
+        a.token = g_token.fetch_add(1, std::memory_order_relaxed) + 1;
         return launched(stq::launch_step_win(a, L->cfg.d_k, L->cfg.d_v, L->mixed, s), "windowed decode step");
+    }
     if (L->cfg.scale_fit == STQ_FIT_LAGGED)
         return launched(stq::launch_step_lagged(a, L->cfg.d_k, L->cfg.d_v, s), "decode step (lagged scales)");
     return launched(stq::launch_step(a, L->cfg.d_k, L->cfg.d_v, L->step_mix, s), "decode step");

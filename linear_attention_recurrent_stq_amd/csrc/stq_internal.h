@@ -73,6 +73,11 @@ struct Args {
     const uint32_t *groups;      // step kernel: [ngroups] head groups, h1 | h2 << 16
     int32_t ngroups;             //   (h2 = 0xffff: a group of one head)
     const float *omega;          // row-impact weights [H * d_k] (nullptr: none)
+    // Windowed layouts: a flag in the pool header that the in-window step sets
+    // to `token` (unique to the call) when one of its states fills its window,
+    // so that the window-end kernel can tell at once that none did.
+    uint64_t *end_flag;
+    uint64_t token;
 };
 
 // Launchers (stq_kernels.hip).  Return the launch's hipError_t.  `mixed`: some

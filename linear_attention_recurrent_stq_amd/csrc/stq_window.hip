@@ -708,8 +708,12 @@ __device__ __forceinline__ void win_tile(const Args &A, const HeadDesc &hd, uint
         A.o[unit * DV + j] = o;
     }
     if (t < DK) dkap[(size_t)n * DK + t] = sm.kr[t];
-    // at the W-th delta the count reaches W; the window-end kernel closes it
-    if (t == 0) *reinterpret_cast<int32_t *>(R + hd.wn) = n + 1;
+    // at the W-th delta the count reaches W; the window-end kernel closes it,
+    // told by the pool's flag holding this call's token
+    if (t == 0) {
+        *reinterpret_cast<int32_t *>(R + hd.wn) = n + 1;
+        if (n + 1 == A.window) *A.end_flag = A.token;
+    }
 }
 
 // Window end of one state holding W deltas: M = fma(g, B + entries, D) with
@@ -845,6 +849,9 @@ __global__ void __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_
 k_win_end(Args A) {
     constexpr int CG = DV / 8;
     __shared__ LdsW<DK, DV> sm;
+    // no state of this call filled its window (the flag holds an earlier
+    // token): one load, and every workgroup is done
+    if (*A.end_flag != A.token) return;
     const size_t unit = blockIdx.x;
     const int b = (int)(unit / (size_t)A.H);
     const int h = (int)(unit - (size_t)b * A.H);

@@ -517,6 +517,58 @@ def test_windowed_mixed_rows_d128():
     _run(w, 40, bits=bits, check_slots_every=8, tag="win-mixed-d128")
 
 
+@pytest.mark.parametrize("d,W", [(64, 4), (128, 16)])
+def test_windowed_staggered_windows(d, W):
+    """Requests whose windows close at different calls: call c steps only the
+    requests b with (b + c) % 3 != 0, so within one call some states fill
+    their window and others do not, and many calls end no window at all (the
+    window-end kernel is told by the pool's flag which calls to skip).  Every
+    unit of 6 x 4 states, outputs at every call and slot bytes every 5 calls,
+    against the oracle."""
+    import torch
+    import oracle
+    import linear_attention_recurrent_stq_amd as stq
+    w = synth.WORKLOADS["windowed_kda"].with_(B=6, H=4, dk=d, dv=d, window=W, comps=10 if d == 64 else 82,
+                                              name=f"win_staggered_d{d}")
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    ocfg = oracle.Cfg.from_workload(w, bits)
+    pool = stq.Pool(L, w.B)
+    slot_of = np.array([3, 0, 5, 1, 4, 2], np.int32)
+    oslots = [ocfg.new_slot() for _ in range(w.B)]
+    bb, hh = np.meshgrid(np.arange(w.B), np.arange(w.H), indexing="ij")
+    M0 = synth.initial_state(w, 0, bb, hh)
+    stq.pack(pool, torch.from_numpy(slot_of).cuda(), torch.from_numpy(M0).cuda())
+    for b in range(w.B):
+        for h in range(w.H):
+            ocfg.pack_head(oslots[b], h, M0[b, h])
+    cv = lambda bits_: torch.from_numpy(np.ascontiguousarray(bits_).view(np.int16)).view(torch.bfloat16).cuda()
+    calls = 3 * W + 6
+    ends = 0
+    for c in range(calls):
+        sub = np.array([b for b in range(w.B) if (b + c) % 3 != 0], np.int64)
+        x = synth.batch_inputs(w, 0, c)
+        ids = torch.from_numpy(slot_of[sub]).cuda()
+        o = torch.empty(len(sub), w.H, w.dv, device="cuda")
+        stq.decode_step(pool, ids, cv(x.q_bits[sub]), cv(x.k_bits[sub]), cv(x.v_bits[sub]),
+                        torch.from_numpy(np.ascontiguousarray(x.a[sub])).cuda(),
+                        torch.from_numpy(np.ascontiguousarray(x.beta[sub])).cuda(), o)
+        got = o.cpu().numpy()
+        ref = []
+        for n, b in enumerate(sub):
+            for h in range(w.H):
+                ref.append(ocfg.step_head(oslots[b], h, x.q[b, h], x.k[b, h], x.v[b, h], x.a[b, h],
+                                          x.beta[b, h]))
+        follow = [(int(b), h) for b in sub for h in range(w.H)]
+        _check_step(got.reshape(-1, w.dv), ref, follow, c, f"staggered-d{d}")
+        ends += sum(1 for b in sub if sum(1 for cc in range(c + 1) if (b + cc) % 3 != 0) % W == 0)
+        if (c + 1) % 5 == 0 or c == calls - 1:
+            allb = pool.slots_view().cpu().numpy()
+            for b in range(w.B):
+                assert np.array_equal(allb[slot_of[b]], oslots[b]), f"slot bytes of request {b} after call {c}"
+    assert ends >= w.B  # every request closed at least one window, at differing calls
+
+
 @pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
 def test_windowed_unequal_head_sizes(dk, dv):
     """Windowed mode at d_k != d_v (uniform 8-bit rows, and rows of mixed
