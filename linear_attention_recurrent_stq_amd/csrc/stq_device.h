@@ -102,21 +102,25 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 // then sits in a branch of its own: a load used inside a branch is waited for
 // there, which would serialise a state's input loads one round trip each.
 // Every such array has an even number of elements and a 4-byte aligned start,
-// so the dword lies inside it.
-__device__ __forceinline__ uint32_t ld_dword(const void *p, int half, size_t e) {
-    return *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p) + (half ? (e >> 1) * 4 : e * 4));
+// so the dword lies inside it.  The address is a base common to the
+// workgroup (scalar registers) plus a 32-bit offset per thread, so a load
+// costs one or two vector instructions of address arithmetic.
+__device__ __forceinline__ uint32_t dword_off(int half, uint32_t e) {
+    return half ? (e & ~1u) * 2u : e * 4u;
 }
-// bf16 (if bf16) or fp32 input element of index parity `odd`
+__device__ __forceinline__ uint32_t ld_dword(const void *p, int half, uint32_t e) {
+    return *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(p) + dword_off(half, e));
+}
+// bf16 (if bf16) or fp32 input element of index parity `odd`: one byte
+// permutation (the bf16 half moved to the top, zeros below, or the dword
+// as it is)
 __device__ __forceinline__ float dec_io(uint32_t d, int bf16, int odd) {
-    const uint32_t h = odd ? (d & 0xffff0000u) : (d << 16);
-    return __uint_as_float(bf16 ? h : d);
+    const uint32_t sel = bf16 ? (odd ? 0x03020c0cu : 0x01000c0cu) : 0x03020100u;
+    return __uint_as_float(__builtin_amdgcn_perm(d, d, sel));
 }
 // fp16 (if f16) or fp32 scale of index parity `odd`
 __device__ __forceinline__ float dec_scale(uint32_t d, int f16, int odd) {
     return f16 ? f16v(odd ? d >> 16 : d) : __uint_as_float(d);
-}
-__device__ __forceinline__ float load1(const void *p, int bf16, size_t e) {
-    return dec_io(ld_dword(p, bf16, e), bf16, (int)(e & 1));
 }
 
 // The per-state inputs thread t reads, for key row t (t < d_k) and value
@@ -143,21 +147,27 @@ __device__ __forceinline__ void keep_lagged(const Inputs &p) {
 template <int DK, int DV, bool LAG = false>
 __device__ __forceinline__ void fetch_inputs(const Args &A, const HeadDesc &hd, const uint8_t *R, size_t unit,
                                              int t, Inputs &p) {
-    const int tk = t < DK ? t : 0, tv = t < DV ? t : 0;
+    const uint32_t tk = t < DK ? t : 0, tv = t < DV ? t : 0;
     p.nr = p.nc = 0;
     if (LAG) {
         // a head without these sections has offset 0 here: inside its region
-        p.nr = ld_dword(R + hd.nrs, A.rs16, t % DK);
-        p.nc = ld_dword(R + hd.ncs, 1, t % DV);
+        p.nr = ld_dword(R + hd.nrs, A.rs16, (uint32_t)t % DK);
+        p.nc = ld_dword(R + hd.ncs, 1, (uint32_t)t % DV);
     }
     p.beta = A.beta[unit];
-    p.a = A.a[A.gate_vec ? unit * DK + tk : unit];
+    // the state's rows of the inputs (uniform), then one offset per thread
+    const size_t es = A.io_bf16 ? 2 : 4;
+    const uint8_t *kb = static_cast<const uint8_t *>(A.k) + unit * (DK * es);
+    const uint8_t *qb = static_cast<const uint8_t *>(A.q) + unit * (DK * es);
+    const uint8_t *vb = static_cast<const uint8_t *>(A.v) + unit * (DV * es);
+    const float *ab = A.a + (A.gate_vec ? unit * DK : unit);
+    p.a = ab[A.gate_vec ? tk : 0u];
     // a head without scales has offset 0 here: still inside its region
     p.r = ld_dword(R + hd.rs, A.rs16, tk);
-    p.k = ld_dword(A.k, A.io_bf16, unit * DK + tk);
-    p.q = ld_dword(A.q, A.io_bf16, unit * DK + tk);
+    p.k = ld_dword(kb, A.io_bf16, tk);
+    p.q = ld_dword(qb, A.io_bf16, tk);
     p.c = ld_dword(R + hd.cs, 1, tv);
-    p.v = ld_dword(A.v, A.io_bf16, unit * DV + tv);
+    p.v = ld_dword(vb, A.io_bf16, tv);
 }
 
 // A head's width and quantized-row count share one descriptor dword; reading

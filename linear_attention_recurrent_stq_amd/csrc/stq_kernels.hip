@@ -168,7 +168,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         sm.g16[t] = g * 0.0625f;
         sm.nog[t] = w < 16 ? -(float)(1 << (w - 1)) * g : 0.0f;
         sm.af[t] = in.a;
-        sm.om[t] = A.omega ? A.omega[hd.rows + t] : 1.0f;
+        if (IMP) sm.om[t] = A.omega[hd.rows + t];  // row-impact weights (read only then)
         sm.kf[t] = dec_io(in.k, A.io_bf16, t & 1);
         sm.qf[t] = dec_io(in.q, A.io_bf16, t & 1);
     }
