@@ -173,9 +173,8 @@ __device__ __forceinline__ void fetch_inputs(const Args &A, const HeadDesc &hd, 
 // A head's width and quantized-row count share one descriptor dword; reading
 // the dword keeps the load on the scalar unit (no 16-bit scalar loads).
 __device__ __forceinline__ uint32_t head_wq(const HeadDesc &hd) {
-    static_assert(offsetof(HeadDesc, width) == 44 && offsetof(HeadDesc, nquant) == 46,
-                  "width and nquant share the 12th dword");
-    return reinterpret_cast<const uint32_t *>(&hd)[11];
+    static_assert(offsetof(HeadDesc, wq) == 44, "width and nquant share the 12th dword");
+    return hd.wq;
 }
 __device__ __forceinline__ int head_width(const HeadDesc &hd) { return (int)(head_wq(hd) & 0xffffu); }
 __device__ __forceinline__ int head_nquant(const HeadDesc &hd) { return (int)(head_wq(hd) >> 16); }
@@ -299,7 +298,7 @@ __device__ __forceinline__ uint4 pack_codes(const float y[8], int w) {
 // reads (a column's partials sit at [j % 8][rg * d_v/8 + j / 8]; a row's at
 // [i % 8][i / 8 * d_v/8 + cg]) over the banks.
 template <int DK, int DV>
-struct Lds {
+struct alignas(16) Lds {
     static constexpr int NT = DK * DV / 64;
     static constexpr int NTP = NT + 4;
     float colp[8][NTP];         // column partial sums: [c][t]
@@ -341,13 +340,22 @@ __device__ __forceinline__ float col_max(const Lds<DK, DV> &sm, int j) {
     return m;
 }
 
+// The d_v/8 partials of a row are contiguous and 16-byte aligned (rows of
+// the array are NTP = NT + 4 floats, a multiple of 4): read four at a time.
 template <int DK, int DV>
 __device__ __forceinline__ float row_max(const Lds<DK, DV> &sm, int i) {
     constexpr int CG = DV / 8;
-    const float *p = &sm.rowm[i & 7][(i >> 3) * CG];
-    float m = p[0];
+    static_assert(CG % 4 == 0 && Lds<DK, DV>::NTP % 4 == 0, "row partials in 16-byte groups");
+    const float4 *p = reinterpret_cast<const float4 *>(&sm.rowm[i & 7][(i >> 3) * CG]);
+    float v[CG];
 #pragma unroll
-    for (int g = 1; g < CG; ++g) m = fmaxf(m, p[g]);
+    for (int g = 0; g < CG / 4; ++g) {
+        const float4 f = p[g];
+        v[4 * g] = f.x; v[4 * g + 1] = f.y; v[4 * g + 2] = f.z; v[4 * g + 3] = f.w;
+    }
+    float m = v[0];
+#pragma unroll
+    for (int g = 1; g < CG; ++g) m = fmaxf(m, v[g]);
     return m;
 }
 
@@ -594,13 +602,15 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
     if (t < DK) {
         const int w = width_of<W>(A, hd, t);
         float ir = 0.0f, rv = 0.0f;
+        uint32_t rh = 0;  // fp16 pattern of the row step (0 for a pivot row)
         bool sat = false;
         if (w != 16) {
             const float Rm = row_max<DK, DV>(sm, t);
             if (A.lagged) reinterpret_cast<float *>(R + hd.srs)[t] = Rm;
             const float rq = div_qmax(Rm, w);
             if (A.rs16) {
-                rv = f16v(h16up(rq));
+                rh = h16up(rq);
+                rv = f16v(rh);
                 sat = rq > 65504.0f;
                 ir = rv > 0.0f ? recip_h(rv) : 0.0f;  // rv is an fp16 value
             } else {
@@ -609,7 +619,7 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
                 if (__builtin_isinf(ir)) ir = 0.0f;
             }
         }
-        if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)h16(rv);
+        if (A.rs16) reinterpret_cast<uint16_t *>(R + hd.rs)[t] = (uint16_t)rh;
         else reinterpret_cast<float *>(R + hd.rs)[t] = rv;
         sm.ir[t] = sat ? -ir : ir;
     }

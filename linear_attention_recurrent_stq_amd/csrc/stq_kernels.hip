@@ -314,9 +314,17 @@ __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
         return;
     }
     uint8_t *S = A.slots + (size_t)slot * A.slot_bytes;
-    const HeadDesc &hd1 = A.heads[h1];
+    // descriptors copied before the first store: the stores into the pool
+    // could alias the table as far as the compiler knows, so fields read
+    // after them would be reloaded with vector loads on the critical path.
+    // The per-row class (MIX 2), lagged scales and row-impact weights keep
+    // reading the table: there the copy would cost spilled registers.
+    constexpr bool COPY = MIX < 2 && !LAG && !IMP;
+    const HeadDesc hd1v = A.heads[h1];
+    const HeadDesc &hd1 = COPY ? hd1v : A.heads[h1];
     if (h2 != 0xffff) {
-        const HeadDesc &hd2 = A.heads[h2];
+        const HeadDesc hd2v = A.heads[h2];
+        const HeadDesc &hd2 = COPY ? hd2v : A.heads[h2];
         const size_t u2 = (size_t)b * A.H + h2;
         Pre4 p1, p2;
         fetch4<DK, DV, LAG>(A, hd1, S + hd1.off, u1, t, rg, cg, p1);
@@ -343,10 +351,12 @@ __device__ __forceinline__ void step_groups(const Args &A, Lds<DK, DV> &sm) {
     }
 }
 
-// The per-row class (MIX 2) is held to four waves per SIMD, the other
-// classes' occupancy: a couple of spilled registers cost less than a wave.
+// The per-row class (MIX 2) and every class at d = 128 are held to four
+// waves per SIMD (128 VGPRs): for the per-row class a couple of spilled
+// registers cost less than a wave.
 template <int DK, int DV, int MIX, bool IMP = false>
-__global__ void __launch_bounds__(DK * DV / 64) __attribute__((amdgpu_waves_per_eu(MIX == 2 ? 4 : 1)))
+__global__ void __launch_bounds__(DK * DV / 64)
+__attribute__((amdgpu_waves_per_eu((MIX == 2 || DK * DV == 128 * 128) ? 4 : 1)))
 k_step(Args A) {
     __shared__ Lds<DK, DV> sm;
     step_groups<DK, DV, MIX, false, IMP>(A, sm);
