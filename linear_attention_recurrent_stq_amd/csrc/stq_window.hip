@@ -858,7 +858,7 @@ k_win_end(Args A) {
     const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
     const int slot = A.slot_ids[b];
     if (slot < 0 || slot >= A.nslots) return;
-    const HeadDesc &hd = A.heads[h];
+    const HeadDesc hd = A.heads[h];  // copied before any store, as in k_win
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     if (*reinterpret_cast<const int32_t *>(R + hd.wn) != A.window) return;
     switch (head_width(hd)) {
@@ -886,11 +886,13 @@ __global__ void __launch_bounds__(DK * DV / 64) k_win(Args A) {
     const int h = (int)(unit - (size_t)b * A.H);
     const int t = threadIdx.x, rg = t / CG, cg = t - rg * CG;
     const int slot = A.slot_ids[b];
+    // the descriptor copied before any store (fields read after a store into
+    // the pool would be reloaded by vector loads)
+    const HeadDesc hd = A.heads[h];
     if (slot < 0 || slot >= A.nslots) {
         if (t < DV) A.o[unit * DV + t] = __builtin_nanf("");
         return;
     }
-    const HeadDesc &hd = A.heads[h];
     uint8_t *R = A.slots + (size_t)slot * A.slot_bytes + hd.off;
     switch (head_width(hd)) {
         case 4: win_tile<DK, DV, 4>(A, hd, R, unit, sm, cix, cvl, kge, qge, t, rg, cg); break;
