@@ -631,12 +631,13 @@ __device__ __forceinline__ void requant_store(const Args &A, const HeadDesc &hd,
 #pragma unroll
     for (int c = 0; c < 8; ++c) scc[c] = 1.0f;
     if (SCALED && per_row<W>()) lds_read8(&sm.cf[8 * cg], scc, 0);
-    // a negative 1/r' marks a saturated row; the minimum finds one in three
-    // min3 operations (a flag per row costs a compare and a select each)
-    float irmin = irr[0];
+    // a negative 1/r' marks a saturated row (1/r' is +0 or positive
+    // otherwise); the OR of the eight sign bits finds one in four or3
+    // operations (a flag per row costs a compare and a select each)
+    uint32_t irsign = __float_as_uint(irr[0]);
 #pragma unroll
-    for (int r = 1; r < 8; ++r) irmin = fminf(irmin, irr[r]);
-    if (__builtin_expect(__any(irmin < 0.0f), 0)) {
+    for (int r = 1; r < 8; ++r) irsign |= __float_as_uint(irr[r]);
+    if (__builtin_expect(__any((int32_t)irsign < 0), 0)) {
         // a row step saturated at 65504: clamp codes to +-qmax
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
