@@ -898,3 +898,62 @@ def test_snapshot_and_resume(name, T):
     fa, fc = straight.slots_view().cpu().numpy(), second.slots_view().cpu().numpy()
     for b in range(w.B):
         assert np.array_equal(fa[b], fc[int(where[b])]), (name, b)
+
+
+# ------------------------------------------------------------ graph replay
+
+@pytest.mark.parametrize("name", ["qwen_gdn", "windowed_kda"])
+def test_decode_step_in_a_replayed_graph(name):
+    """stq_decode_step captured once in a HIP graph and replayed step after
+    step (fresh inputs copied in between, eager work and a synchronization
+    between replays) gives, at every replay, the same outputs as the same
+    call made eagerly on a twin pool, and the same slot bytes at the end.
+    Windowed layout (W = 4): the captured call keeps one token, so after its
+    first window end the pool's flag holds that token at every replay and
+    every window-end workgroup checks its state's count."""
+    import torch
+    import linear_attention_recurrent_stq_amd as stq
+    over = dict(B=4, H=4, layers=1, name=f"graph_{name}")
+    if name == "windowed_kda":
+        over.update(dk=64, dv=64, window=4, comps=10)
+    w = synth.WORKLOADS[name].with_(**over)
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    eager, graphed = stq.Pool(L, w.B), stq.Pool(L, w.B)
+    ids = torch.tensor([2, 0, 3, 1], dtype=torch.int32, device="cuda")
+    if w.init != "zero":
+        bb, hh = np.meshgrid(np.arange(w.B), np.arange(w.H), indexing="ij")
+        M0 = torch.from_numpy(synth.initial_state(w, 0, bb, hh)).cuda()
+        stq.pack(eager, ids, M0)
+        stq.pack(graphed, ids, M0)
+    io = torch.bfloat16 if w.io == "bf16" else torch.float32
+    q = torch.empty(w.B, w.H, w.dk, dtype=io, device="cuda")
+    k = torch.empty_like(q)
+    v = torch.empty(w.B, w.H, w.dv, dtype=io, device="cuda")
+    a = torch.empty((w.B, w.H, w.dk) if w.gate == "keyvec" else (w.B, w.H), device="cuda")
+    beta = torch.empty(w.B, w.H, device="cuda")
+    o_e = torch.empty(w.B, w.H, w.dv, device="cuda")
+    o_g = torch.empty_like(o_e)
+
+    def load(t):
+        x = synth.batch_inputs(w, 0, t)
+        cv = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+        q.copy_(cv(x.q_bits)); k.copy_(cv(x.k_bits)); v.copy_(cv(x.v_bits))
+        a.copy_(torch.from_numpy(x.a)); beta.copy_(torch.from_numpy(x.beta))
+
+    load(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stq.decode_step(graphed, ids, q, k, v, a, beta, o_g)
+    torch.cuda.synchronize()
+    steps = 3 * w.window + 2 if w.window > 1 else 12
+    for t in range(steps):
+        load(t)
+        stq.decode_step(eager, ids, q, k, v, a, beta, o_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_g), f"{name}: replay {t} differs from the eager call"
+    assert torch.equal(eager.slots_view(), graphed.slots_view()), f"{name}: slot bytes differ"
+    print(f"[graph] {name}: {steps} replays identical to the eager calls", flush=True)
