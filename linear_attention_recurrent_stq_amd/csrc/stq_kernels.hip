@@ -132,15 +132,16 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         for (int r = 0; r < 8; ++r)
             raw[r] = make_uint4(*reinterpret_cast<const uint32_t *>(R + rw.base + (uint32_t)r * (DV / 2) + 4 * cg), 0, 0, 0);
     } else if (W == kW4P) {
+        // the piece of the block's first pivot row, loaded once ahead of the
+        // 4-bit rows (a load per row into one register set would make each
+        // wait for every load before it)
+        pr = rw.m8 ? __builtin_ctz(rw.m8) : -1;
+        if (pr >= 0) pv = load_piece(R + row_o<DV, W>(rw, pr), cg, 16);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             raw[r] = make_uint4(0, 0, 0, 0);
-            if (row_w<W>(rw, r) != 16) {
+            if (row_w<W>(rw, r) != 16)
                 raw[r].x = *reinterpret_cast<const uint32_t *>(R + row_o<DV, W>(rw, r) + 4 * cg);
-            } else if (pr < 0) {
-                pv = load_piece(R + row_o<DV, W>(rw, r), cg, 16);
-                pr = r;
-            }
         }
     } else {
 #pragma unroll
