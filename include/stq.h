@@ -126,7 +126,9 @@ typedef struct {
  * Otherwise dev_bytes must be >= that size; the table header is uploaded and
  * every slot is set to the empty state (zero state, cumulative gates 1, no
  * deltas), asynchronously on `stream`.  Slot s starts at
- * base + header_bytes + s * slot_bytes.
+ * base + header_bytes + s * slot_bytes.  Windowed layouts keep an 8-byte
+ * window-end flag at the end of the header, written by stq_decode_step: the
+ * header of such a pool is not read-only while it is stepped.
  */
 stq_status stq_alloc_pool(const stq_layout *layout, int32_t slots, void *dev_base,
                           size_t dev_bytes, void *stream, stq_pool *out);
@@ -143,6 +145,10 @@ stq_status stq_alloc_pool(const stq_layout *layout, int32_t slots, void *dev_bas
  * Per state: dequantize, decay, w = (a*S)k, u = beta(v - w), S += u k^T,
  * o = S q, refit column then row scales, requantize and write back (windowed:
  * append the delta; requantize at the window end).  B may be 0 (no-op).
+ * The call allocates nothing and does not synchronize, so it may be captured
+ * in a HIP graph; a replayed windowed call reuses its captured token, which
+ * costs the window-end kernel a per-state check on every replay but changes
+ * no result.
  */
 stq_status stq_decode_step(const stq_pool *pool, int32_t B, const int32_t *d_slot_ids,
                            const void *d_q, const void *d_k, const void *d_v,
