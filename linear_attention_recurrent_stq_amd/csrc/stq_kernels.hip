@@ -143,15 +143,26 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
             if (row_w<W>(rw, r) != 16)
                 raw[r].x = *reinterpret_cast<const uint32_t *>(R + row_o<DV, W>(rw, r) + 4 * cg);
         }
-    } else {
+    } else if (W == 0) {
+        // per-row widths: each piece read as the two aligned dwords around it
+        // and shifted into place without a branch on the row's width (a load
+        // consumed inside such a branch waits for every load in flight).
+        // A 4-bit piece reads 4 bytes past it at most: the next row, or the
+        // row scales that follow the code rows of a head with quantized rows.
+        // FP16 pivot rows (16 bytes a piece, rare) are loaded when they are
+        // dequantized (here the row's first two dwords, unused), so the block
+        // holds at most 8 bytes a row.
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            // per-row widths: FP16 pivot rows (16 bytes a piece, rare) are
-            // loaded when they are dequantized, so the block holds at most 8
-            // bytes a row
-            if (W == 0 && row_w<W>(rw, r) == 16) raw[r] = make_uint4(0, 0, 0, 0);
-            else raw[r] = load_piece(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r));
+            const int w = row_w<W>(rw, r);
+            const uint32_t off = (uint32_t)(w == 16 ? 0 : w) * (uint32_t)cg;
+            const uint32_t *q = reinterpret_cast<const uint32_t *>(R + (row_o<DV, W>(rw, r) + (off & ~3u)));
+            const uint32_t lo = q[0], hi = q[1], sh = (off & 3u) * 8u;  // shift 0 or 16 bits
+            raw[r] = make_uint4(__builtin_amdgcn_alignbit(hi, lo, sh), hi >> sh, 0, 0);
         }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) raw[r] = load_piece(R + row_o<DV, W>(rw, r), cg, row_w<W>(rw, r));
     }
 
     // per key row and per value column constants, computed once per state
