@@ -130,7 +130,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
     } else if (W == kW4P && fw) {
 #pragma unroll
         for (int r = 0; r < 8; ++r)
-            raw[r] = make_uint4(*reinterpret_cast<const uint32_t *>(R + rw.base + (uint32_t)r * (DV / 2) + 4 * cg), 0, 0, 0);
+            raw[r] = make_uint4(*reinterpret_cast<const uint32_t *>(R + (rw.base + (uint32_t)r * (DV / 2) + 4u * (uint32_t)cg)), 0, 0, 0);
     } else if (W == kW4P) {
         // the piece of the block's first pivot row, loaded once ahead of the
         // 4-bit rows (a load per row into one register set would make each
@@ -141,7 +141,7 @@ __device__ __forceinline__ void step_tile(const Args &A, const HeadDesc &hd, uin
         for (int r = 0; r < 8; ++r) {
             raw[r] = make_uint4(0, 0, 0, 0);
             if (row_w<W>(rw, r) != 16)
-                raw[r].x = *reinterpret_cast<const uint32_t *>(R + row_o<DV, W>(rw, r) + 4 * cg);
+                raw[r].x = *reinterpret_cast<const uint32_t *>(R + (row_o<DV, W>(rw, r) + 4u * (uint32_t)cg));
         }
     } else if (W == 0) {
         // per-row widths: each piece read as the two aligned dwords around it
