@@ -85,6 +85,23 @@ def test_header_holds_the_head_groups(stq, name):
     assert L.header_bytes == _header_bytes(w.H, w.dk, per_head)
 
 
+@pytest.mark.parametrize("H,d", [(32, 128), (64, 64)])
+def test_windowed_header_holds_the_window_end_flag(stq, H, d):
+    """Windowed layouts keep an 8-byte window-end flag after the tables (at
+    an 8-byte boundary), inside the header: at H = 64, d = 64 the tables fill
+    whole 256-byte blocks, so the flag takes one more block."""
+    w = synth.WORKLOADS["windowed_kda"].with_(H=H, dk=d, dv=d, comps=20, name=f"win_hdr_{H}_{d}")
+    bits = synth.unit_bits(w)
+    L = stq.Layout.from_workload(w, bits)
+    n = 64 * H + 4 * H * d + 4 * H          # descriptors, row table, one group per 8-bit head
+    want = ((n + 7) // 8 * 8 + 8 + 255) // 256 * 256
+    assert L.header_bytes == want
+    plain = stq.Layout.from_workload(w.with_(window=1, comps=0, name=f"step_hdr_{H}_{d}"), bits)
+    assert plain.header_bytes == (n + 255) // 256 * 256
+    if n % 256 == 0:
+        assert L.header_bytes == plain.header_bytes + 256
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("H", 0, 1), ("d_k", 96, 2), ("d_v", 32, 2), ("unit", 5, 1), ("gate", 2, 1),
     ("row_scale", 0, 1), ("col_scale", 1, 1), ("io_dtype", 2, 1), ("window", 0, 1),
